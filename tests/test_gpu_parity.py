@@ -1,0 +1,211 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Inputs come from the seeded generator; expected values come only from the
+oracle.  Packing and unpacking are bit-exact; products meet the row-rms
+relative error bound TOL = 2e-3 (fp32 accumulation against fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fwht_rotation_sqrt_amd as tb
+import oracle
+import synth
+from gpu_util import TOL, act_dev, act_f64, dev, f16_ulp_distance, host, note, scales_dev, signs_dev
+
+pytestmark = pytest.mark.gpu
+
+PACK_REF = {"2bit": oracle.pack_2bit, "base3": oracle.pack_base3}
+PACK_GPU = {"2bit": tb.tb_pack_2bit, "base3": tb.tb_pack_base3}
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 1024), (37, 5120), (5, 17408), (17408, 5120)])
+def test_pack_unpack_bitexact(packing, n, k):
+    note(f"pack/unpack {packing} n={n} k={k}")
+    t = synth.trits(synth.rng(200, 0, n % 251, k // 128), n, k)
+    ref, bad = PACK_REF[packing](t)
+    assert bad == 0
+    bad_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    packed = PACK_GPU[packing](dev(t), bad_count=bad_d)
+    assert np.array_equal(host(packed), ref)
+    assert int(host(bad_d)[0]) == 0
+    back = tb.tb_unpack(packing, packed, k, bad_count=bad_d)
+    assert np.array_equal(host(back), t)
+    assert int(host(bad_d)[0]) == 0
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_pack_invalid_inputs_counted(packing):
+    note(f"pack invalid {packing}")
+    n, k = 4, 256
+    t = synth.trits(synth.rng(201, 0), n, k)
+    t[0, 3] = 2
+    t[2, 100] = -7
+    t[3, 255] = 5
+    ref, bad = PACK_REF[packing](t)
+    assert bad == 3
+    bad_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    packed = PACK_GPU[packing](dev(t), bad_count=bad_d)
+    assert np.array_equal(host(packed), ref) and int(host(bad_d)[0]) == 3
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_unpack_invalid_codes_counted(packing):
+    note(f"unpack invalid {packing}")
+    n, k = 3, 384
+    t = synth.trits(synth.rng(202, 0), n, k)
+    p, _ = PACK_REF[packing](t)
+    if packing == "2bit":
+        p[0, 5] = 0xFF          # four 11 codes
+        p[2, 90] = 0x3C         # two 11 codes
+    else:
+        p[0, 5] = 250           # >= 243
+        p[1, 25] = 95           # last byte of group 0 with pad digits (0, 1)
+        p[2, 51] = 243
+    want, bad = (oracle.unpack_2bit if packing == "2bit" else oracle.unpack_base3)(p, k)
+    bad_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = tb.tb_unpack(packing, dev(p), k, bad_count=bad_d)
+    assert np.array_equal(host(got), want)
+    assert int(host(bad_d)[0]) == bad and bad > 0
+
+
+# ------------------------------------------------------------------ rotation
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,k", [(1, 1024), (1, 5120), (3, 17408), (512, 5120)])
+def test_rotate_fp32_out(x_dtype, rows, k):
+    note(f"rotate {x_dtype}->f32 rows={rows} k={k}")
+    g = synth.rng(210, 0, rows % 251, k // 1024)
+    oc = synth.outlier_channels(g, k)
+    x = synth.activations(g, rows, k, oc, x_dtype)
+    sb = synth.sign_bits(synth.rng(210, synth.T_SIGNS), k)
+    want = oracle.rotate(act_f64(x, x_dtype), sb)
+    got = host(tb.tb_fwht_rotate(act_dev(x, x_dtype), signs_dev(sb), torch.float32)).astype(np.float64)
+    scale = np.sqrt(np.mean(want * want, axis=1, keepdims=True))
+    assert np.max(np.abs(got - want) / scale) < 2e-6
+
+
+@pytest.mark.parametrize("rows,k", [(1, 5120), (512, 5120), (7, 17408)])
+def test_rotate_fp16_out_within_one_ulp(rows, k):
+    note(f"rotate bf16->f16 rows={rows} k={k}")
+    g = synth.rng(211, 0, rows % 251, k // 1024)
+    x = synth.activations(g, rows, k, synth.outlier_channels(g, k), "bf16")
+    sb = synth.sign_bits(synth.rng(211, synth.T_SIGNS), k)
+    want = oracle.rotate(act_f64(x, "bf16"), sb).astype(np.float16)   # round to nearest even
+    got = host(tb.tb_fwht_rotate(act_dev(x, "bf16"), signs_dev(sb), torch.float16))
+    d = f16_ulp_distance(got, want)
+    assert d.max() <= 1
+    assert np.mean(d) < 1e-3
+
+
+def test_rotate_in_place_and_fp16_input():
+    note("rotate in place f32 and f16->f32")
+    k, rows = 2048, 5
+    g = synth.rng(212, 0)
+    x = synth.activations(g, rows, k, None, "f32")
+    sb = synth.sign_bits(synth.rng(212, synth.T_SIGNS), k)
+    want = oracle.rotate(x.astype(np.float64), sb)
+    xd = dev(x)
+    tb.tb_fwht_rotate(xd, signs_dev(sb), out=xd)
+    assert np.max(np.abs(host(xd) - want)) < 1e-5
+    x16 = x.astype(np.float16)
+    want16 = oracle.rotate(x16.astype(np.float64), sb)
+    got = host(tb.tb_fwht_rotate(dev(x16), signs_dev(sb), torch.float32))
+    assert np.max(np.abs(got - want16)) < 1e-5
+
+
+# ------------------------------------------------------------------ decode product
+
+def _linear(wid, n, k, rows, x_dtype, outliers, layer=0, linear=0):
+    li = synth.linear_inputs(wid, n, k, rows, x_dtype, outliers, layer, linear)
+    return li
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 1024), (16, 1024), (37, 2048), (130, 5120), (1000, 1024)])
+@pytest.mark.parametrize("xr_dtype", [torch.float32, torch.float16])
+def test_gemv_small_shapes(packing, n, k, xr_dtype):
+    note(f"gemv {packing} n={n} k={k} xr={xr_dtype}")
+    g = synth.rng(220, 0, n % 251, k // 128)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    xr = g.standard_normal((8, k)).astype(np.float32)
+    if xr_dtype == torch.float16:
+        xr = xr.astype(np.float16)
+    packed, _ = PACK_REF[packing](t)
+    want = oracle.gemv(packing, packed, s, xr.astype(np.float64), k)
+    pd, sd, xd = dev(packed), scales_dev(s), dev(xr)
+    for b in (1, 2, 5, 8):
+        got = host(tb.tb_gemv(packing, pd, sd, xd[:b].contiguous()))
+        assert got.shape == (b, n)
+        assert oracle.rel_err(got, want[:b]) < TOL
+
+
+def _e2e_gemv(wid, packing, n, k, x_dtype, outliers, batches, layer=0, linear=0):
+    li = _linear(wid, n, k, max(batches), x_dtype, outliers, layer, linear)
+    ref_packed, _ = PACK_REF[packing](li.trits)
+    packed = PACK_GPU[packing](dev(li.trits))
+    assert np.array_equal(host(packed), ref_packed)
+    x64 = act_f64(li.x, x_dtype)
+    want = oracle.gemv(packing, ref_packed, li.scales, oracle.rotate(x64, li.signs), k)
+    sd, sgn, xd = scales_dev(li.scales), signs_dev(li.signs), act_dev(li.x, x_dtype)
+    errs = {}
+    for b in batches:
+        xr = tb.tb_fwht_rotate(xd[:b].contiguous(), sgn, torch.float32)
+        y = host(tb.tb_gemv(packing, packed, sd, xr))
+        errs[b] = oracle.rel_err(y, want[:b])
+        assert errs[b] < TOL, (b, errs[b])
+    return errs
+
+
+def test_linear1024_2bit_b1_end_to_end():
+    note("1024x1024 2-bit batch 1, fp32 activations")
+    _e2e_gemv(0, "2bit", 1024, 1024, "f32", False, (1,))
+
+
+def test_gemv_ffn_base3_b1_end_to_end():
+    note("17408x5120 base-3 batch 1, bf16 activations with outliers")
+    _e2e_gemv(1, "base3", synth.FFN, synth.HIDDEN, "bf16", True, (1,))
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("li", range(len(synth.BLOCK_LINEARS)), ids=[l.name for l in synth.BLOCK_LINEARS])
+def test_block_linears_b1_b8(packing, li):
+    lin = synth.BLOCK_LINEARS[li]
+    note(f"block linear {lin.name} {lin.n}x{lin.k} {packing} batch 1 and 8")
+    _e2e_gemv(2, packing, lin.n, lin.k, "bf16", False, (1, 8), 0, li)
+
+
+# ------------------------------------------------------------------ prefill product
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 37, 1024), (64, 64, 256), (100, 300, 2048), (130, 1000, 5120)])
+def test_gemm_small_shapes(m, n, k):
+    note(f"gemm m={m} n={n} k={k}")
+    g = synth.rng(230, 0, m % 251, n % 251)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    xr = g.standard_normal((m, k)).astype(np.float16)
+    packed, _ = oracle.pack_2bit(t)
+    want = oracle.gemm("2bit", packed, s, xr.astype(np.float64), k)
+    got = host(tb.tb_gemm("2bit", dev(packed), scales_dev(s), dev(xr)))
+    assert oracle.rel_err(got, want) < TOL
+
+
+def test_gemm_pp512_end_to_end():
+    note("pp512 GEMM M=512 N=17408 K=5120 2-bit, bf16 activations with outliers")
+    m, n, k = 512, synth.FFN, synth.HIDDEN
+    li = _linear(3, n, k, m, "bf16", True)
+    ref_packed, _ = oracle.pack_2bit(li.trits)
+    packed = tb.tb_pack_2bit(dev(li.trits))
+    assert np.array_equal(host(packed), ref_packed)
+    xr_exact = oracle.rotate(act_f64(li.x, "bf16"), li.signs)
+    want = oracle.gemm("2bit", ref_packed, li.scales, xr_exact.astype(np.float16).astype(np.float64), k)
+    xr = tb.tb_fwht_rotate(act_dev(li.x, "bf16"), signs_dev(li.signs), torch.float16)
+    y = host(tb.tb_gemm("2bit", packed, scales_dev(li.scales), xr))
+    assert oracle.rel_err(y, want) < TOL
+    # against the unrounded product too: fp16 rounding of X' stays inside the bound
+    want_exact = oracle.gemm("2bit", ref_packed, li.scales, xr_exact, k)
+    assert oracle.rel_err(y, want_exact) < TOL
