@@ -125,7 +125,8 @@ def _linear(wid, n, k, rows, x_dtype, outliers, layer=0, linear=0):
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
-@pytest.mark.parametrize("n,k", [(1, 128), (3, 1024), (16, 1024), (37, 2048), (130, 5120), (1000, 1024)])
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 1024), (16, 1024), (37, 2048), (130, 5120), (1000, 1024),
+                                 (7, 640), (50, 1152), (300, 3200), (81, 17408)])
 @pytest.mark.parametrize("xr_dtype", [torch.float32, torch.float16])
 def test_gemv_small_shapes(packing, n, k, xr_dtype):
     note(f"gemv {packing} n={n} k={k} xr={xr_dtype}")
