@@ -4,14 +4,14 @@
 // reach 1.76 bit" (g128 fp16 scales, unpack and scale fused in the product)
 // and section "Throughput" (decode streams the packed weights once per token).
 //
-// The weights never become fp16.  Each ternary code c = t + 1 in {0, 1, 2} is
-// used directly as an fp4 (e2m1) matrix-core operand: the nibble c encodes
-// c / 2, so sum_k t_k x_k = 2 sum_k (c_k / 2) x_k - sum_k x_k.
-//   * 2-bit codes: a dword of 16 codes splits into two dwords of 8 nibbles with
-//     one AND (and one shift): the 2-bit fields already are the nibble values.
-//   * base-3 bytes: one LDS table lookup turns a byte into a dword holding its
-//     five base-3 digits as nibbles (the table has 32 bank-spread copies so a
-//     wave's lookups do not conflict).
+// The weights never become fp16: they enter the matrix cores as fp4 (e2m1).
+//   * 2-bit codes c = t + 1 in {0, 1, 2}: the 2-bit field already is the
+//     nibble of c / 2, so a dword of 16 codes splits into two operand dwords
+//     with one AND (and one shift), and sum_k t_k x_k = 2 sum_k (c_k / 2) x_k
+//     - sum_k x_k (the activation sum is kept per group).
+//   * base-3 bytes: one LDS table lookup turns a byte into a dword holding the
+//     nibbles of its five trits themselves (-1.0, 0, +1.0); the table has 32
+//     bank-spread copies so a wave's lookups do not conflict.
 // The activations become three fp8 (e4m3) limbs per element, per 128-group
 // scaled by a power of two so the largest magnitude lies in [128, 256):
 //   x * 2^sig = l0 + l1/16 + l2/256, each limb the e4m3 rounding of what is
@@ -19,16 +19,15 @@
 // One v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 weight rows by 128
 // K-slots; its A rows are (batch, limb) pairs (row 4b + limb), so one matrix
 // instruction serves up to four batch rows.  Per group the limbs are combined
-// in fp32, the sum of the group's activations is subtracted, and the fp16
-// scale and 2^-sig are applied, all in fp32.
+// in fp32 and the fp16 scale and 2^-sig applied, in fp32.
 //
-// Work split: a workgroup of kWaves waves; each wave owns a tile of 16 weight
-// rows over all of K.  The packed tile streams through registers kDepth
-// stages ahead (a stage is 8 groups = 1024 weights per row), is written to a
-// per-wave LDS buffer with coalesced 16-byte loads, and is read back in the
-// matrix-core operand layout.  The workgroup prepares the activation limbs
-// for as many groups as fit in LDS, with two barriers per such chunk (one
-// chunk covers all of K at batch 1 for K up to 5120 x 2).
+// Work split: a workgroup of up to 16 waves holds rt tiles of 16 weight rows;
+// the 8-group stages (1024 weights per row) of a tile are split over ks waves.
+// A wave's packed bytes stream through registers kDepth stages ahead with
+// coalesced 16-byte buffer loads, go to a per-wave LDS buffer and are read
+// back in the operand layout.  A few "prep" waves turn the activations into
+// limbs in LDS (for as many groups as fit; larger K takes several launches)
+// while the other waves already stream weights.
 #include "tb_internal.hpp"
 
 #include <mutex>
@@ -38,27 +37,53 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;       // waves per workgroup
 constexpr int kDepth = 2;           // staged stages in flight per wave (registers)
 constexpr int kStageGroups = 8;     // groups per stage (1024 weights per row)
-constexpr int kCopies = 32;         // bank-spread copies of the base-3 table
+constexpr int kCopies = 32;         // bank-spread copies of the base-3 table (one per half-wave lane)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kTeam = 16;           // threads preparing one (batch, group) of activations
 constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past any buffer: reads zero
 
+// LDS layouts below keep the rows that 16 consecutive lanes read in distinct
+// 4-byte banks (or on the same dword); the base-3 table is spread over 32
+// lanes, as bank-conflict counters show lanes 16 apart colliding.
 template <int PACK>
 struct Fmt {
   static constexpr int kGroupBytes = PACK == 0 ? 32 : kB3GroupBytes;
   static constexpr int kMfmas = PACK == 0 ? 1 : 2;             // matrix instructions per group
-  static constexpr int kRowStage = kGroupBytes * kStageGroups;  // 256 or 208 bytes
+  static constexpr int kRowStage = kGroupBytes * kStageGroups;  // 256 or 208 bytes of a row per stage
+  // LDS row stride: 66 or 54 dwords, so the 16 rows a quarter-wave reads
+  // (two dwords each) fall in distinct banks
+  static constexpr int kRowLds = kRowStage + 8;
   static constexpr int kChunksPerRow = kRowStage / 16;          // 16 or 13
   static constexpr int kStageChunks = 16 * kChunksPerRow;       // 256 or 208
   static constexpr int kLoads = (kStageChunks + 63) / 64;       // 4
-  static constexpr int kScaleOff = 16 * kRowStage + 32;         // + pad for operand over-reads
-  static constexpr int kStageLds = kScaleOff + 16 * 16;         // + the stage's scales [16 rows][8]
-  static constexpr int kTable = PACK == 1 ? 256 * kCopies * 4 : 0;
+  static constexpr int kStageLds = 16 * kRowLds + 32;           // + pad for operand over-reads
+  // base-3 table: entry e at byte 256 e, copy c (lane & 15) at + 4c, so one
+  // byte permute forms the address (e << 8) | 4c from the staged bytes
+  static constexpr int kTable = PACK == 1 ? 256 * 256 : 0;
 };
+
+// Activation limb rows in LDS: 128 K-slot bytes padded to 36 dwords so the
+// three limb rows of a batch start in different banks.
+constexpr int kARow = 144;
+constexpr int kAGroup = 3 * kARow;   // one batch's three limb rows
+
+// Limb block of batch b: [ng groups][instructions per group][kAGroup], so the
+// offset of a group inside it is a compile-time constant.  The stride between
+// batches is padded to 48 mod 128 bytes (as kAGroup is) so the rows of the
+// four batches one instruction reads start in different banks.
+__host__ __device__ constexpr int a_batch_stride(int ng, int mfmas) {
+  const int base = ng * mfmas * kAGroup;
+  return base + (48 - base % 128 + 128) % 128;
+}
+// Bytes of the per-(batch, group) factor region, rounded to 16, plus 16 for
+// the workgroup's ready counter.
+__host__ __device__ constexpr int f_region_bytes(int nb, int ng) { return ((nb * ng * 8 + 15) & ~15) + 16; }
 
 // K-slot of trit tau (0..127) of a group, and which matrix instruction of the
 // group it belongs to.  B operand: lane group q supplies slots 32q..32q+31.
@@ -81,20 +106,42 @@ __device__ __forceinline__ int slot_of(int tau, int* mi) {
   }
 }
 
+// LDS of a workgroup, in this order: the base-3 table (at address 0, so a
+// table address needs no base), the activation limbs, the per-(batch, group)
+// factors, then the waves' staging buffers.
 // A operand slot s of lane group q' reads K-slot 16q'+s (s < 16) or 64+16q'+s-16.
 struct Smem {
+  uint8_t* lds;     // LDS address 0: the base-3 table, 256 entries x 256 bytes
+  uint8_t* a;       // [B][ng][mfmas][3][144] activation limbs in K-slot order
+  int a_bstride;    // bytes between batches in a
+  float2* f;        // [B][ng] = {2^-sig, sum of reconstructed activations}
+  int ng;           // groups of this launch
+  int* ready;       // count of prep waves done (after f)
   uint8_t* stage;   // waves x kStageLds (reused for the K-part reduction at the end)
-  uint32_t* table;  // 256 x kCopies (base-3)
-  uint8_t* a;       // [ng][mfmas][B][3][128] activation limbs in K-slot order
-  float2* f;        // [ng][B] = {2^-sig, sum of reconstructed activations}
 };
 
-__device__ __forceinline__ uint32_t base3_nibbles(uint32_t e) {
+// LDS reads at a plain byte address.  The kernel declares no static LDS, so
+// its dynamic LDS starts at address 0; building addresses as integers lets
+// constant offsets fold into the instructions' offset field.
+// (The constant offset is added to the pointer, not the integer, so the
+// compiler knows the sum does not wrap and may fold it.)
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+template <typename T, int OFF = 0>
+__device__ __forceinline__ T lds_read(uint32_t addr) {
+  lds_u8* p = reinterpret_cast<lds_u8*>(static_cast<uintptr_t>(addr)) + OFF;
+  return *reinterpret_cast<__attribute__((address_space(3))) const T*>(p);
+}
+
+// Table entry of a base-3 byte: its five digits d, low digit first, as e2m1
+// nibbles of the trit t = d - 1 (-1.0 = 0xA, 0 = 0x0, +1.0 = 0x2); bytes
+// above 242 are not codes and read as five zero trits.
+__device__ __forceinline__ uint32_t base3_t_nibbles(uint32_t e) {
   if (e >= 243u) return 0u;
   uint32_t v = 0;
 #pragma unroll
   for (int d = 0; d < 5; ++d) {
-    v |= (e % 3u) << (4 * d);
+    const uint32_t digit = e % 3u;
+    v |= (digit == 0u ? 0xAu : digit == 2u ? 0x2u : 0x0u) << (4 * d);
     e /= 3u;
   }
   return v;
@@ -105,167 +152,335 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
 }
 
-// Eight consecutive activations of batch row b, group g (absolute), from lane
-// (tid % 16) of a team.
-template <int XDT>
-__device__ __forceinline__ void load_x8(const void* __restrict__ xr, int k, int b, int g, int l16, float x[8]) {
-  const int64_t base = int64_t(b) * k + int64_t(g) * kGroup + 8 * l16;
-  if constexpr (XDT == 0) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xr) + base);
-    const float4 u = p[0], v = p[1];
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-  } else {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xr) + base);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Elements of a (batch, group) that thread l16 of its team of 16 converts:
+//   2-bit: 8 consecutive elements 8 l16 ..; they land in two limb dwords.
+//   base-3: the 10 digits of code bytes 2 l16 and 2 l16 + 1 (elements 10 l16
+//   ..; those past 127 are the pad digits, taken as 0), one 16-byte block of
+//   each limb row.  Threads 13..15 cover bytes 26..31 with zeros, so every
+//   K-slot the matrix instructions read is written.
+template <int PACK>
+struct XMap {
+  static constexpr int kElems = PACK == 0 ? 8 : 10;
+  static __device__ __forceinline__ int first(int l16) { return PACK == 0 ? 8 * l16 : 10 * l16; }
+};
+
+template <int XDT, int PACK>
+__device__ __forceinline__ void load_x(const void* __restrict__ xr, int k, int b, int g, int l16, float (&x)[10]) {
+  const int64_t row = int64_t(b) * k + int64_t(g) * kGroup;
+  const int first = XMap<PACK>::first(l16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = float(__builtin_bit_cast(_Float16, uint16_t(w[i] & 0xFFFFu)));
-      x[2 * i + 1] = float(__builtin_bit_cast(_Float16, uint16_t(w[i] >> 16)));
+  for (int e = 0; e < 5; ++e) {
+    if (2 * e >= XMap<PACK>::kElems) {
+      x[2 * e] = x[2 * e + 1] = 0.f;
+      continue;
     }
+    const int idx = first + 2 * e;
+    const int ic = min(idx, kGroup - 2);  // in-bounds address; the value is dropped below
+    float2 v;
+    if constexpr (XDT == 0) {
+      v = *reinterpret_cast<const float2*>(static_cast<const float*>(xr) + row + ic);
+    } else {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(xr) + row + ic);
+      v.x = float(__builtin_bit_cast(_Float16, uint16_t(u & 0xFFFFu)));
+      v.y = float(__builtin_bit_cast(_Float16, uint16_t(u >> 16)));
+    }
+    const bool ok = idx < kGroup;
+    x[2 * e] = ok ? v.x : 0.f;
+    x[2 * e + 1] = ok ? v.y : 0.f;
   }
 }
 
-// Split eight activations of one (batch, group) into three e4m3 limbs at the
-// group's power-of-two scale and write them to their K-slots; lane 0 of the
-// team records {2^-sig, sum of the reconstructed values}.  The limb values
-// are decoded back from the stored bytes, so the residuals are exact whatever
-// the conversion's rounding.
+// Butterfly reductions over the 16 lanes of a DPP row (a team), no LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+// The four e4m3 bytes of d as floats, to a[first + stride * i].
+template <int FIRST, int STRIDE>
+__device__ __forceinline__ void fp8x4_to_f32(int d, float (&a)[10]) {
+  a[FIRST] = __builtin_amdgcn_cvt_f32_fp8(d, 0);
+  a[FIRST + STRIDE] = __builtin_amdgcn_cvt_f32_fp8(d, 1);
+  a[FIRST + 2 * STRIDE] = __builtin_amdgcn_cvt_f32_fp8(d, 2);
+  a[FIRST + 3 * STRIDE] = __builtin_amdgcn_cvt_f32_fp8(d, 3);
+}
+
+// Split a thread's elements of one (batch, group) into three e4m3 limbs at
+// the group's power-of-two scale and store them in their K-slots; lane 0 of
+// the team records {2^-sig, sum of the reconstructed values}.  The limb
+// values are decoded back from the stored bytes, so the residuals are exact
+// whatever the conversion's rounding.
 template <int PACK>
-__device__ __forceinline__ void limbs_for_group(const Smem& sm, int nb, int b, int g, int l16, const float x[8]) {
-  constexpr int M = Fmt<PACK>::kMfmas;
+__device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, int l16, const float (&x)[10]) {
+  constexpr int E = XMap<PACK>::kElems;
   float mx = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[i]));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kTeam));
+  for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(x[e]));
+  mx = row16_max(mx);
   int sig = 0;
   if (mx > 0.f) {
-    int e;
-    frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-    sig = 8 - e;     // mx * 2^sig in [128, 256)
+    int ex;
+    frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+    sig = 8 - ex;     // mx * 2^sig in [128, 256)
   }
+  float cur[10];
+#pragma unroll
+  for (int e = 0; e < 10; ++e) cur[e] = ldexpf(x[e], sig);
   float sum = 0.f;
+  uint8_t* rowbase;
+  int off;
+  if constexpr (PACK == 0) {
+    rowbase = sm.a + b * sm.a_bstride + g * kAGroup;
+    off = 32 * (l16 >> 2) + 16 * ((l16 & 3) >> 1) + 4 * (l16 & 1);
+  } else {
+    const int p0 = 2 * l16, mi = p0 >> 4, pp = p0 & 15;
+    rowbase = sm.a + b * sm.a_bstride + (g * 2 + mi) * kAGroup;
+    off = 32 * (pp >> 2) + 8 * (pp & 3);
+  }
+  constexpr float kW[3] = {1.f, 0.0625f, 0.00390625f};
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const float xa = ldexpf(x[i], sig), xb = ldexpf(x[i + 1], sig);
-    const int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(xa, xb, 0, false);
-    const float a0 = __builtin_amdgcn_cvt_f32_fp8(p0, 0), b0 = __builtin_amdgcn_cvt_f32_fp8(p0, 1);
-    const float ra = (xa - a0) * 16.f, rb = (xb - b0) * 16.f;
-    const int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, 0, false);
-    const float a1 = __builtin_amdgcn_cvt_f32_fp8(p1, 0), b1 = __builtin_amdgcn_cvt_f32_fp8(p1, 1);
-    const float sa = (ra - a1) * 16.f, sb = (rb - b1) * 16.f;
-    const int p2 = __builtin_amdgcn_cvt_pk_fp8_f32(sa, sb, 0, false);
-    const float a2 = __builtin_amdgcn_cvt_f32_fp8(p2, 0), b2 = __builtin_amdgcn_cvt_f32_fp8(p2, 1);
-    sum += (a0 + a1 * 0.0625f + a2 * 0.00390625f) + (b0 + b1 * 0.0625f + b2 * 0.00390625f);
+  for (int limb = 0; limb < 3; ++limb) {
+    float a[10];
+    uint8_t* dst = rowbase + limb * kARow + off;
+    if constexpr (PACK == 0) {
+      // even elements -> slots off..off+3, odd elements -> off+8..off+11
+      int de = __builtin_amdgcn_cvt_pk_fp8_f32(cur[0], cur[2], 0, false);
+      de = __builtin_amdgcn_cvt_pk_fp8_f32(cur[4], cur[6], de, true);
+      int dd = __builtin_amdgcn_cvt_pk_fp8_f32(cur[1], cur[3], 0, false);
+      dd = __builtin_amdgcn_cvt_pk_fp8_f32(cur[5], cur[7], dd, true);
+      fp8x4_to_f32<0, 2>(de, a);
+      fp8x4_to_f32<1, 2>(dd, a);
+      a[8] = a[9] = 0.f;
+      *reinterpret_cast<uint32_t*>(dst) = uint32_t(de);
+      *reinterpret_cast<uint32_t*>(dst + 8) = uint32_t(dd);
+    } else {
+      // byte 2 l16: digits in slots off..off+4, byte 2 l16 + 1: off+8..off+12;
+      // slots 5..7 of each 8-slot block hold zero
+      int d0 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[0], cur[1], 0, false);
+      d0 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[2], cur[3], d0, true);
+      const int d1 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[4], 0.f, 0, false);
+      int d2 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[5], cur[6], 0, false);
+      d2 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[7], cur[8], d2, true);
+      const int d3 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[9], 0.f, 0, false);
+      fp8x4_to_f32<0, 1>(d0, a);
+      fp8x4_to_f32<5, 1>(d2, a);
+      a[4] = __builtin_amdgcn_cvt_f32_fp8(d1, 0);
+      a[9] = __builtin_amdgcn_cvt_f32_fp8(d3, 0);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(uint32_t(d0), uint32_t(d1), uint32_t(d2), uint32_t(d3));
+    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int mi;
-      const int slot = slot_of<PACK>(8 * l16 + i + h, &mi);
-      uint8_t* row = sm.a + ((((g * M + mi) * nb + b) * 3) << 7) + slot;
-      row[0] = uint8_t(p0 >> (8 * h));
-      row[128] = uint8_t(p1 >> (8 * h));
-      row[256] = uint8_t(p2 >> (8 * h));
+    for (int e = 0; e < 10; ++e) {
+      if constexpr (PACK == 0) sum = fmaf(a[e], kW[limb], sum);
+      cur[e] = (cur[e] - a[e]) * 16.f;
     }
   }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, kTeam);
-  if (l16 == 0) sm.f[g * nb + b] = make_float2(ldexpf(1.f, -sig), sum);
+  if constexpr (PACK == 0) sum = row16_sum(sum);  // only the 2-bit path needs it
+  if (l16 == 0) sm.f[b * sm.ng + g] = make_float2(ldexpf(1.f, -sig), sum);
 }
 
 // ---------------------------------------------------------------- matrix work
 
-// B operand(s) of group g for row (lane & 15) from the staged bytes, then one
-// (2-bit) or two (base-3) instructions per row set.
-template <int PACK, int NR>
-__device__ __forceinline__ void group_mfma(const Smem& sm, const uint8_t* stage, int rb, int g, int gc, int nb,
-                                           v4f out[NR]) {
-  using F = Fmt<PACK>;
-  const int lane = threadIdx.x & 63, nl = lane & 15, q = lane >> 4;
-  const int a_limb = nl & 3, a_bq = nl >> 2;
-  v8i bop[F::kMfmas];
+// Per-lane constants of the matrix work.
+struct LaneCtx {
+  int b_row;      // byte offset of this lane's staged row and K-part (B operand)
+  int a_lane[2];  // per row set: LDS address of this lane's A-operand row in group 0
+  int f_lane[2];  // per row set: index of this lane's batch row in f
+  uint32_t tab;   // base-3 table: this lane's copy offset 4 * (lane & 15) in byte 0
+};
+
+// Raw staged bytes of group g for this lane, from bo = b_row + group-bytes *
+// (the even group of the pair) and the group's parity P.
+//   2-bit: the two dwords of its 32 codes;
+//   base-3: the aligned dword pairs around its 4-byte pieces of the two
+//   instructions (odd groups start 2 bytes into a dword; realigned in make_bop).
+template <int PACK, int P>
+__device__ __forceinline__ void read_group_bytes(uint32_t bo, uint32_t (&raw)[4]) {
   if constexpr (PACK == 0) {
-    const uint2 w = *reinterpret_cast<const uint2*>(stage + nl * rb + 32 * g + 8 * q);
-    const uint32_t m = 0x33333333u;
-    bop[0] = v8i{int(w.x & m), int((w.x >> 2) & m), int(w.y & m), int((w.y >> 2) & m), 0, 0, 0, 0};
+    const u32x2 w = lds_read<u32x2, 32 * P>(bo);
+    raw[0] = w.x; raw[1] = w.y; raw[2] = 0; raw[3] = 0;
   } else {
+    // rows are only 4-byte aligned here: dword-pair reads
+    constexpr int o = P ? kB3GroupBytes - 2 : 0;
+    raw[0] = lds_read<uint32_t, o>(bo);
+    raw[1] = lds_read<uint32_t, o + 4>(bo);
+    raw[2] = lds_read<uint32_t, o + 16>(bo);
+    raw[3] = lds_read<uint32_t, o + 20>(bo);
+  }
+}
+
+// B operand(s) from the raw bytes of a group of parity P.
+//   * 2-bit: the 2-bit codes already are e2m1 nibbles for c/2; even and odd
+//     codes of each dword go to separate dwords.
+//   * base-3: one table lookup per byte; the address (byte << 8) | copy is
+//     formed by one byte permute.  Bytes past the group's 26 (and the two pad
+//     digits of byte 25) meet all-zero activation slots, and fp4 has no NaN,
+//     so they add 0.  Nibbles 5..7 of each looked-up dword are zero.
+template <int PACK, int P>
+__device__ __forceinline__ void make_bop(const Smem& sm, const LaneCtx& lc, const uint32_t (&raw)[4],
+                                         v8i (&bop)[Fmt<PACK>::kMfmas]) {
+  if constexpr (PACK == 0) {
+    const uint32_t m = 0x33333333u;
+    bop[0] = v8i{int(raw[0] & m), int((raw[0] >> 2) & m), int(raw[1] & m), int((raw[1] >> 2) & m), 0, 0, 0, 0};
+  } else {
+    const uint32_t by[2] = {__builtin_amdgcn_alignbyte(raw[1], raw[0], 2 * P),
+                            __builtin_amdgcn_alignbyte(raw[3], raw[2], 2 * P)};
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-      const int o = nl * rb + kB3GroupBytes * g + 16 * mi + 4 * q;
-      const uint32_t* p32 = reinterpret_cast<const uint32_t*>(stage + (o & ~3));
-      const uint32_t bytes = __builtin_amdgcn_alignbyte(p32[1], p32[0], uint32_t(o & 3));
       int dw[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t e = (bytes >> (8 * w)) & 0xFFu;
-        uint32_t v = sm.table[e * kCopies + (lane & (kCopies - 1))];
-        if (mi == 1 && 4 * q + w >= kB3GroupBytes - 16) v = 0;
-        dw[w] = int(v);
+        // address bytes: [0] = lane copy offset, [1] = code byte w, [2..3] = 0
+        const uint32_t addr = __builtin_amdgcn_perm(lc.tab, by[mi], 0x0C0C0004u | (uint32_t(w) << 8));
+        dw[w] = lds_read<int>(addr);
       }
       bop[mi] = v8i{dw[0], dw[1], dw[2], dw[3], 0, 0, 0, 0};
     }
   }
+}
+
+// A operands of group gc (lane rows of unused (batch, limb) pairs read a
+// valid limb row: row i of A only feeds row i of the result, never stored).
+template <int PACK, int NR>
+__device__ __forceinline__ void load_aop(const LaneCtx& lc, int gc, v8i (&aops)[NR][Fmt<PACK>::kMfmas]) {
+  using F = Fmt<PACK>;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t ag = uint32_t(lc.a_lane[r] + gc * F::kMfmas * kAGroup);
+    const u32x4 lo0 = lds_read<u32x4, 0>(ag), hi0 = lds_read<u32x4, 64>(ag);
+    aops[r][0] = v8i{int(lo0.x), int(lo0.y), int(lo0.z), int(lo0.w), int(hi0.x), int(hi0.y), int(hi0.z), int(hi0.w)};
+    if constexpr (F::kMfmas == 2) {
+      const u32x4 lo1 = lds_read<u32x4, kAGroup>(ag), hi1 = lds_read<u32x4, kAGroup + 64>(ag);
+      aops[r][1] = v8i{int(lo1.x), int(lo1.y), int(lo1.z), int(lo1.w), int(hi1.x), int(hi1.y), int(hi1.z), int(hi1.w)};
+    }
+  }
+}
+
+template <int PACK, int NR>
+__device__ __forceinline__ void group_mma(const v8i (&aops)[NR][Fmt<PACK>::kMfmas],
+                                          const v8i (&bop)[Fmt<PACK>::kMfmas], v4f (&out)[NR]) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     v4f a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mi = 0; mi < F::kMfmas; ++mi) {
-      v8i aop = {0, 0, 0, 0, 0, 0, 0, 0};
-      const int b = 4 * r + a_bq;
-      if (a_limb < 3 && b < nb) {
-        const uint8_t* ap = sm.a + ((((gc * F::kMfmas + mi) * nb + b) * 3 + a_limb) << 7) + 16 * q;
-        const uint4 lo = *reinterpret_cast<const uint4*>(ap);
-        const uint4 hi = *reinterpret_cast<const uint4*>(ap + 64);
-        aop = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-      }
-      a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[mi], a4, 0, 4, 0, 127, 0, 127);
-    }
+    for (int mi = 0; mi < Fmt<PACK>::kMfmas; ++mi)
+      a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aops[r][mi], bop[mi], a4, 0, 4, 0, 127, 0, 127);
     out[r] = a4;
   }
-  // keep the next group's operand loads from being hoisted above this point
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Epilogue of one group.  D rows 4*(lane/16)+i: this lane holds batch 4r + q,
-// limbs i = 0..2.  Branch-free on purpose: a matrix instruction must run with
-// the whole wave active, so its result may not feed a lane-divergent block.
-template <int NR>
-__device__ __forceinline__ void group_epilogue(const Smem& sm, const v4f acc[NR], float sc, int gc, int nb,
-                                               float yacc[NR]) {
-  const int q = (threadIdx.x & 63) >> 4;
+// Epilogue constants of group gc for this lane's batches: c = s 2^-sig, and
+// for 2-bit codes c = 2 s 2^-sig (the factor 2 turns the nibble values c/2
+// back into codes) with the activation-sum correction -s 2^-sig S added to
+// yacc at once.  The group's
+// fp16 scale is half P of sq0 (the stage's scales of the lane's row, two per
+// dword, advanced one dword per group pair: indexing a register array with
+// the loop counter would put it in scratch memory).
+template <int PACK, int NR, int P>
+__device__ __forceinline__ void group_consts(const Smem& sm, const LaneCtx& lc, uint32_t sq0, int gc,
+                                             float (&c)[NR], float (&yacc)[NR]) {
+  const float sc = float(__builtin_bit_cast(_Float16, uint16_t(P ? sq0 >> 16 : sq0 & 0xFFFFu)));
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int b = 4 * r + q;
-    const float2 fs = sm.f[gc * nb + min(b, nb - 1)];
-    const float p = acc[r][0] + acc[r][1] * 0.0625f + acc[r][2] * 0.00390625f;
-    const float contrib = (sc * fs.x) * fmaf(2.f, p, -fs.y);
-    yacc[r] += b < nb ? contrib : 0.f;
+    const float2 fs = sm.f[lc.f_lane[r] + gc];
+    const float cg = sc * fs.x;
+    if constexpr (PACK == 0) {
+      c[r] = 2.f * cg;
+      yacc[r] = fmaf(-cg, fs.y, yacc[r]);
+    } else {
+      c[r] = cg;  // base-3 operands are the trits themselves
+    }
   }
 }
 
-// fp16 scale of group g of row (lane & 15) from the stage's LDS copy
-template <int PACK>
-__device__ __forceinline__ float scale_of(const uint8_t* stage, int g) {
-  const int nl = threadIdx.x & 15;
-  return float(*reinterpret_cast<const _Float16*>(stage + Fmt<PACK>::kScaleOff + 16 * nl + 2 * g));
-}
-
-// All groups of one staged block (sg <= 8 groups).  A rolled loop on purpose:
-// unrolling lets the compiler hoist every group's operand loads at once and
-// run out of registers.  The epilogue of group g-1 runs after the
-// instructions of group g are issued, hiding the matrix-core latency.
-template <int PACK, int NR>
-__device__ __forceinline__ void stage_compute(const Smem& sm, const uint8_t* stage, int rb, int sg, int gc0,
-                                              int nb, float yacc[NR]) {
-  v4f prev[NR], cur[NR];
-  group_mfma<PACK, NR>(sm, stage, rb, 0, gc0, nb, prev);
-#pragma unroll 1
-  for (int g = 1; g < sg; ++g) {
-    group_mfma<PACK, NR>(sm, stage, rb, g, gc0 + g, nb, cur);
-    group_epilogue<NR>(sm, prev, scale_of<PACK>(stage, g - 1), gc0 + g - 1, nb, yacc);
+// y += c * (d0 + d1/16 + d2/256) with d the limb rows of this lane's result
+// (batch 4r + q).  Lanes of batches >= nb accumulate values that are never
+// stored.  No branch here on purpose: a matrix instruction must run with the
+// whole wave active, so its result may not feed a lane-divergent block.
+template <int NR>
+__device__ __forceinline__ void group_epilogue(const v4f (&acc)[NR], const float (&c)[NR], float (&yacc)[NR]) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) prev[r] = cur[r];
+  for (int r = 0; r < NR; ++r) {
+    const float p = fmaf(acc[r][2], 0.00390625f, fmaf(acc[r][1], 0.0625f, acc[r][0]));
+    yacc[r] = fmaf(c[r], p, yacc[r]);
   }
-  group_epilogue<NR>(sm, prev, scale_of<PACK>(stage, sg - 1), gc0 + sg - 1, nb, yacc);
+}
+
+// Pipeline state of one stage's group loop.
+template <int PACK, int NR>
+struct GroupPipe {
+  uint32_t raw[2][4];                  // staged bytes of the next groups, by parity
+  v4f prev[NR];                        // matrix results of the previous group
+  float cprev[NR];                     // its epilogue factors
+};
+
+// One group of parity P: B operands from bytes read one group earlier, the A
+// operands and epilogue constants, the next group's bytes, the matrix
+// instructions, then the previous group's epilogue.  So every dependent LDS
+// round trip except the table lookup is a group ahead of its use.
+template <int PACK, int NR, int P>
+__device__ __forceinline__ void group_step(const Smem& sm, const LaneCtx& lc, uint32_t bo, int gc,
+                                           uint32_t sq0, GroupPipe<PACK, NR>& st, float (&yacc)[NR]) {
+  using F = Fmt<PACK>;
+  __builtin_amdgcn_sched_barrier(0);
+  v8i bop[F::kMfmas];
+  make_bop<PACK, P>(sm, lc, st.raw[P], bop);
+  v8i aops[NR][F::kMfmas];
+  load_aop<PACK, NR>(lc, gc, aops);
+  // the next group's bytes (past the stage's last group: the row padding, ignored)
+  if constexpr (P == 0) read_group_bytes<PACK, 1>(bo, st.raw[1]);
+  else read_group_bytes<PACK, 0>(bo + 2 * F::kGroupBytes, st.raw[0]);
+  float ccur[NR];
+  group_consts<PACK, NR, P>(sm, lc, sq0, gc, ccur, yacc);
+  v4f cur[NR];
+  group_mma<PACK, NR>(aops, bop, cur);
+  group_epilogue<NR>(st.prev, st.cprev, yacc);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.prev[r] = cur[r];
+    st.cprev[r] = ccur[r];
+  }
+}
+
+// All groups of one staged block of sg (1..8) groups, two per iteration of a
+// rolled loop (unrolled further, the compiler hoists later groups' loads and
+// runs out of registers).
+template <int PACK, int NR>
+__device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg,
+                                              int gc0, const uint32_t (&sreg)[4], float (&yacc)[NR]) {
+  using F = Fmt<PACK>;
+  GroupPipe<PACK, NR> st;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.prev[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    st.cprev[r] = 0.f;
+  }
+  uint32_t sq[4] = {sreg[0], sreg[1], sreg[2], sreg[3]};
+  uint32_t bo = stage + lc.b_row;
+  read_group_bytes<PACK, 0>(bo, st.raw[0]);
+  int g = 0;
+#pragma unroll 1
+  for (; g + 1 < sg; g += 2) {
+    group_step<PACK, NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
+    group_step<PACK, NR, 1>(sm, lc, bo, gc0 + g + 1, sq[0], st, yacc);
+    bo += 2 * F::kGroupBytes;
+    sq[0] = sq[1];
+    sq[1] = sq[2];
+    sq[2] = sq[3];
+  }
+  if (g < sg) group_step<PACK, NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
+  group_epilogue<NR>(st.prev, st.cprev, yacc);
 }
 
 // ---------------------------------------------------------------- streaming
@@ -303,6 +518,10 @@ __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wrs, __amdgpu
 #pragma unroll
     for (int i = 0; i < 4; ++i) sreg[i] = __builtin_amdgcn_alignbyte(wd[i + 1], wd[i], sh);
   }
+  // keep each stage's loads together and in stage order: the waits before a
+  // stage's use count outstanding loads, so a later stage's load scheduled
+  // ahead of this one would be waited for as well
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -314,7 +533,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // One full stage: registers -> this wave's LDS buffer, matrix work, then
 // refill the same register slot with stage s + kDepth.
 template <int PACK, int NR, bool ALIGNED>
-__device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, __amdgpu_buffer_rsrc_t wrs,
+__device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, uint32_t stage_addr, const LaneCtx& lc,
+                                          __amdgpu_buffer_rsrc_t wrs,
                                           __amdgpu_buffer_rsrc_t srs, const uint32_t (&src)[Fmt<PACK>::kLoads],
                                           uint32_t srow_scale, int s, int s_end, int nb,
                                           uint4 (&regs)[Fmt<PACK>::kLoads], uint32_t (&sreg)[4],
@@ -325,12 +545,17 @@ __device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, __a
 #pragma unroll
   for (int j = 0; j < F::kLoads; ++j) {
     const int c = 64 * j + lane;
-    if (c < F::kStageChunks) reinterpret_cast<uint4*>(my_stage)[c] = regs[j];
+    if (c < F::kStageChunks) {
+      // chunk c = row c / chunks-per-row, 16-byte column c % chunks-per-row; rows are
+      // 8-byte aligned at the padded stride, so two 8-byte writes
+      const int r = c / F::kChunksPerRow;
+      uint2* dst = reinterpret_cast<uint2*>(my_stage + r * F::kRowLds + 16 * (c - r * F::kChunksPerRow));
+      dst[0] = make_uint2(regs[j].x, regs[j].y);
+      dst[1] = make_uint2(regs[j].z, regs[j].w);
+    }
   }
-  if (lane < 16)
-    *reinterpret_cast<uint4*>(my_stage + F::kScaleOff + 16 * lane) = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
   wave_lds_fence();
-  stage_compute<PACK, NR>(sm, my_stage, F::kRowStage, kStageGroups, s * kStageGroups, nb, yacc);
+  stage_compute<PACK, NR>(sm, stage_addr, lc, kStageGroups, s * kStageGroups, sreg, yacc);
   issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s + kDepth, s_end, regs, sreg);
 }
 
@@ -348,7 +573,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     float* __restrict__ y, int nb, int n, int k, int g_begin, int ng, int accumulate, int rt, int ks) {
   using F = Fmt<PACK>;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index through readfirstlane: per-wave quantities below become
+  // scalar (SALU) work instead of vector work
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nthreads = 64 * rt * ks;
   const int groups = k / kGroup;
   const int row_bytes = F::kGroupBytes * groups;
@@ -357,22 +584,50 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   const int nl = lane & 15, q = lane >> 4;
 
   Smem sm;
-  sm.stage = smem;
-  sm.table = reinterpret_cast<uint32_t*>(smem + rt * ks * F::kStageLds);
-  sm.a = reinterpret_cast<uint8_t*>(sm.table) + F::kTable;
-  const int a_bytes = ng * F::kMfmas * nb * 3 * 128;
+  sm.lds = smem;
+  sm.a = smem + F::kTable;
+  sm.a_bstride = a_batch_stride(ng, F::kMfmas);
+  const int a_bytes = nb * sm.a_bstride;
   sm.f = reinterpret_cast<float2*>(sm.a + a_bytes);
+  sm.ng = ng;
+  sm.ready = reinterpret_cast<int*>(sm.a + a_bytes + f_region_bytes(nb, ng) - 16);
+  sm.stage = sm.a + a_bytes + f_region_bytes(nb, ng);
   uint8_t* my_stage = sm.stage + wave * F::kStageLds;
-
-  // ---- activations of this thread's first (batch, group): loads go out first
-  const int team = tid / kTeam, l16 = tid % kTeam, nteams = nthreads / kTeam;
-  const int pairs = ng * nb;
-  float xv[8];
-  {
-    const int pr = team < pairs ? team : 0;
-    const int g = pr / nb, b = pr - g * nb;
-    load_x8<XDT>(xr, k, b, g_begin + g, l16, xv);
+  const uint32_t my_stage_addr = uint32_t(F::kTable + a_bytes + f_region_bytes(nb, ng) + wave * F::kStageLds);
+  LaneCtx lc;
+  lc.b_row = nl * F::kRowLds + (PACK == 0 ? 8 * q : 4 * q);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    // A rows are 4b + limb; unused rows (limb 3, or batch >= nb) read a valid
+    // limb row instead (they only feed result rows that are never read)
+    const int limb = min(nl & 3, 2), b = min(4 * r + (nl >> 2), nb - 1);
+    lc.a_lane[r] = F::kTable + b * sm.a_bstride + limb * kARow + 16 * q;
+    lc.f_lane[r] = min(4 * r + q, nb - 1) * ng;
   }
+  lc.tab = uint32_t(4 * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
+
+  // ---- roles.  The first prep_waves waves build the activation limbs (and
+  // the base-3 table) and only then load weights; the others start the weight
+  // stream at once.  A wave starts its matrix work when the LDS counter shows
+  // every prep wave done, not at a workgroup barrier, so it never waits for
+  // another wave's weight loads to be issued.
+  const int pairs = ng * nb;
+  const int nwaves = rt * ks;
+  const int prep_waves = min(nwaves, (pairs + 11) / 12);  // ~3 (batch, group) pairs per team
+  const bool prep = wave < prep_waves;
+  const int team = tid / kTeam, l16 = tid % kTeam, nteams = prep_waves * (64 / kTeam);
+  float xa[10], xb[10], xc[10];
+  if (prep) {
+    // the activation loads go out before any weight load of the workgroup
+    // (loads return in order, so whatever is issued behind the weight stream
+    // arrives after it)
+    const int p0 = team, p1 = team + nteams, p2 = team + 2 * nteams;
+    if (p0 < pairs) load_x<XDT, PACK>(xr, k, p0 % nb, g_begin + p0 / nb, l16, xa);
+    if (p1 < pairs) load_x<XDT, PACK>(xr, k, p1 % nb, g_begin + p1 / nb, l16, xb);
+    if (p2 < pairs) load_x<XDT, PACK>(xr, k, p2 % nb, g_begin + p2 / nb, l16, xc);
+  }
+  if (tid == 0) *sm.ready = 0;
+  __syncthreads();
 
   // ---- this wave's stages: [s_lo, s_hi); only the launch's last stage may be partial
   const int nst = (ng + kStageGroups - 1) / kStageGroups;
@@ -394,31 +649,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
 
   uint4 stg[kDepth][F::kLoads];
   uint32_t scl[kDepth][4];
+  if (prep) {
+    if constexpr (PACK == 1) {
+      for (int e = tid; e < 256; e += 64 * prep_waves) {
+        const uint32_t v = base3_t_nibbles(uint32_t(e));
+        uint4* dst = reinterpret_cast<uint4*>(sm.lds + 256 * e);
+#pragma unroll
+        for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
+      }
+    }
+    const int p0 = team, p1 = team + nteams, p2 = team + 2 * nteams;
+    if (p0 < pairs) limbs_for_group<PACK>(sm, p0 % nb, p0 / nb, l16, xa);
+    if (p1 < pairs) limbs_for_group<PACK>(sm, p1 % nb, p1 / nb, l16, xb);
+    if (p2 < pairs) limbs_for_group<PACK>(sm, p2 % nb, p2 / nb, l16, xc);
+    for (int pr = team + 3 * nteams; pr < pairs; pr += nteams) {
+      load_x<XDT, PACK>(xr, k, pr % nb, g_begin + pr / nb, l16, xa);
+      limbs_for_group<PACK>(sm, pr % nb, pr / nb, l16, xa);
+    }
+    // this wave's LDS writes complete before its count is seen
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
     issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s_lo + d, s_full, stg[d], scl[d]);
+  // every prep wave has finished (each adds 1 exactly once, and none waits
+  // on anything, so this ends)
+  while (__hip_atomic_load(sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < prep_waves)
+    __builtin_amdgcn_s_sleep(1);
 
-  // ---- workgroup set-up while the weights stream in
-  if constexpr (PACK == 1) {
-    for (int e = tid; e < 256; e += nthreads) {
-      const uint32_t v = base3_nibbles(uint32_t(e));
-      uint4* dst = reinterpret_cast<uint4*>(sm.table + e * kCopies);
-#pragma unroll
-      for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
-    }
-  }
-  for (int i = tid; i < a_bytes / 16; i += nthreads) reinterpret_cast<uint4*>(sm.a)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-  if (team < pairs) {
-    const int g = team / nb, b = team - g * nb;
-    limbs_for_group<PACK>(sm, nb, b, g, l16, xv);
-  }
-  for (int pr = team + nteams; pr < pairs; pr += nteams) {
-    const int g = pr / nb, b = pr - g * nb;
-    load_x8<XDT>(xr, k, b, g_begin + g, l16, xv);
-    limbs_for_group<PACK>(sm, nb, b, g, l16, xv);
-  }
-  __syncthreads();
 
   float yacc[NR];
 #pragma unroll
@@ -429,14 +688,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   for (; s + kDepth <= s_full; s += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
-      run_stage<PACK, NR, ALIGNED>(sm, my_stage, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d], scl[d],
-                                   yacc);
+      run_stage<PACK, NR, ALIGNED>(sm, my_stage, my_stage_addr, lc, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d],
+                                   scl[d], yacc);
   }
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)
     if (s + d < s_full)
-      run_stage<PACK, NR, ALIGNED>(sm, my_stage, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d], scl[d],
-                                   yacc);
+      run_stage<PACK, NR, ALIGNED>(sm, my_stage, my_stage_addr, lc, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d],
+                                   scl[d], yacc);
 
   if (has_tail) {
     // partial last stage: fewer groups, 2-byte granular loads straight to LDS
@@ -450,17 +709,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
       if (row0 + r < n)
         v = *reinterpret_cast<const uint16_t*>(packed + (row0 + r) * row_bytes +
                                                (g_begin + s_full * kStageGroups) * F::kGroupBytes + 2 * cc);
-      reinterpret_cast<uint16_t*>(my_stage)[c] = v;
+      *reinterpret_cast<uint16_t*>(my_stage + r * F::kRowLds + 2 * cc) = v;
     }
     uint32_t h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       h[i] = (i < sg && srow_scale != kNoLoad) ? scales[srow_scale + s_full * kStageGroups + i] : 0u;
-    if (lane < 16)
-      *reinterpret_cast<uint4*>(my_stage + F::kScaleOff + 16 * lane) =
-          make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    const uint32_t hw[4] = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     wave_lds_fence();
-    stage_compute<PACK, NR>(sm, my_stage, rb, sg, s_full * kStageGroups, nb, yacc);
+    stage_compute<PACK, NR>(sm, my_stage_addr, lc, sg, s_full * kStageGroups, hw, yacc);
   }
 
   // ---- add the ks partial sums of each tile (through the staging buffers)
@@ -495,18 +752,24 @@ Plan make_plan(int b, int n, int k) {
   using F = Fmt<PACK>;
   const int tiles = (n + 15) / 16;
   const int groups = k / kGroup;
+  const int per_group = F::kMfmas * b * kAGroup + b * 8;  // + b * 127 bytes of batch padding
   // smallest tiles-per-workgroup that keeps the grid within one workgroup per CU
   int rt = 1;
   while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
-  // groups per launch: activation limbs of all launches' groups must fit in LDS
-  const int fixed = kMaxWaves * F::kStageLds + F::kTable;
-  const int per_group = F::kMfmas * b * 3 * 128 + b * 8;
-  int ng = (kLdsBytes - fixed) / per_group;
-  ng = ng / kStageGroups * kStageGroups;  // >= 8 for every batch <= 8
+  // K-part waves per tile, then the groups per launch whose activation limbs
+  // fit in what LDS has left; fewer K-part waves leave room for more groups.
+  // At one wave per tile the room is always enough for >= 8 groups (batch <= 8).
+  int ks = kMaxWaves / rt, ng = 0;
+  for (; ks >= 1; --ks) {
+    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 127 - 31;
+    ng = room > 0 ? room / per_group : 0;
+    if (ng >= kStageGroups || ks == 1) break;
+  }
+  if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
   if (ng > groups) ng = groups;
   const int nst = (ng + kStageGroups - 1) / kStageGroups;
-  int ks = kMaxWaves / rt;
   if (ks > nst) ks = nst;
+  if (ks < 1) ks = 1;
   return Plan{rt, ks, ng};
 }
 
@@ -516,6 +779,7 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, f
   using F = Fmt<PACK>;
   const int groups = k / kGroup;
   const Plan pl = make_plan<PACK>(b, n, k);
+  if (pl.ng < 1) return;  // unreachable for batch <= 8 (see make_plan); never loop without progress
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_kernel<PACK, NR, XDT, ALIGNED>),
@@ -523,12 +787,11 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, f
   });
   const int tiles = (n + 15) / 16;
   const unsigned grid = unsigned((tiles + pl.rt - 1) / pl.rt);
-  const int per_group = F::kMfmas * b * 3 * 128 + b * 8;
   for (int g0 = 0; g0 < groups; g0 += pl.ng) {
     const int ng = groups - g0 < pl.ng ? groups - g0 : pl.ng;
     const int nst = (ng + kStageGroups - 1) / kStageGroups;
     const int ks = pl.ks < nst ? pl.ks : nst;
-    const int lds = pl.rt * ks * F::kStageLds + F::kTable + ng * per_group;
+    const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) + pl.rt * ks * F::kStageLds;
     gemv_mfma_kernel<PACK, NR, XDT, ALIGNED><<<grid, 64 * pl.rt * ks, lds, s>>>(
         packed, scales, xr, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks);
   }
