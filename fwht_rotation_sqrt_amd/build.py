@@ -24,6 +24,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function"]
+# Per-file device flags.  The prefill product keeps 136 accumulators per lane
+# live across its K loop; in the accumulation-register form the compiler
+# copies them between registers around every matrix instruction, in the
+# VGPR form it updates them in place.
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -48,7 +53,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return _run([hipcc, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj])
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        return _run([hipcc, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj])
 
     jobs = jobs or min(len(sources), os.cpu_count() or 4, 8)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:

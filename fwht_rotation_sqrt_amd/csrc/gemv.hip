@@ -576,7 +576,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   // the wave index through readfirstlane: per-wave quantities below become
   // scalar (SALU) work instead of vector work
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int nthreads = 64 * rt * ks;
   const int groups = k / kGroup;
   const int row_bytes = F::kGroupBytes * groups;
   const int tile = wave / ks, kp = wave - tile * ks;
