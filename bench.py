@@ -45,7 +45,27 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for calibrating HBM byte counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "tb_gemv_base3_17408x5120_b1_traffic.md")
+
+
+def gemv_traffic_bytes():
+    """HBM bytes per GEMV launch from the committed counter runs, or None when the
+    kernel source has changed since they were taken (or they are missing)."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_FILE) if l.startswith("machine-readable:"))
+        rec = json.loads(line.split(":", 1)[1])
+        src = open(os.path.join(HERE, rec["source"]), "rb").read()
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def dev(a):
@@ -197,6 +217,15 @@ def main():
               "(the path would shard W by output rows across GPUs, see the design notes)", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
+    if args.copy_calibration:
+        # a known amount of HBM traffic: 256 MiB read + 256 MiB written per copy
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 5}), flush=True)
+        return
     tb.library()
     d = decode_setup()
     wall, t_gemv, t_rot = bench_decode(d, args.steps, args.warmup)
@@ -204,6 +233,7 @@ def main():
     per_copy = d["per_copy"]
     value = per_copy / (wall / args.steps) / 1e9
     gemv_gbs = per_copy / t_gemv / 1e9
+    traffic = gemv_traffic_bytes()
     gemm = None if args.no_gemm else bench_gemm(args.steps)
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
     rec = {
@@ -224,7 +254,11 @@ def main():
                    "weight_copies": d["copies"], "step": "tb_fwht_rotate(bf16->f32) + tb_gemv",
                    "hip_graph": True, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     # counter-measured HBM bytes of one launch over the same launch time
+                     "traffic": None if traffic is None else round(traffic / t_gemv / 1e9, 2),
+                     "traffic_bytes_per_launch": traffic,
+                     "algorithmic_bytes_per_launch": per_copy,
                      "kernel": "tb_gemv base-3 17408x5120 b1", "kernel_us": round(t_gemv * 1e6, 3)},
         "rotate_us_b1_k5120": round(t_rot * 1e6, 3),
         "rotate_share_of_step": round(t_rot / (wall / args.steps), 4),
