@@ -22,7 +22,7 @@ TB_GEMV_MAX_BATCH = 8
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",
-           "tb_gemv", "tb_gemm", "tb_status_string", "tb_last_hip_error")
+           "tb_gemv", "tb_linear", "tb_gemm", "tb_status_string", "tb_last_hip_error")
 
 _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGNATURES = {
@@ -32,6 +32,7 @@ _SIGNATURES = {
     "tb_unpack": (_INT, [_INT, _VP, _I64, _I64, _VP, _VP, _VP]),
     "tb_fwht_rotate": (_INT, [_VP, _INT, _VP, _INT, _I64, _I64, _VP, _VP]),
     "tb_gemv": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _I64, _I64, _I64, _VP]),
+    "tb_linear": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_gemm": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_status_string": (ctypes.c_char_p, [_INT]),
     "tb_last_hip_error": (ctypes.c_char_p, []),
@@ -165,6 +166,22 @@ def tb_gemv(packing, packed, scales, xr, y=None, stream=None):
     _check(y, "y", (torch.float32,))
     _call("tb_gemv", _packing(packing), _ptr(packed), _ptr(scales), _ptr(xr), _ACT_DT[xr.dtype],
           _ptr(y), b, n, k, _stream(stream))
+    return y
+
+
+def tb_linear(packing, packed, scales, x, sign_bits, y=None, stream=None):
+    """y[B][N] = packed ternary W times R_K x, x[B][K] unrotated (rotation inside the call)."""
+    _check(packed, "packed", (torch.uint8,))
+    _check(scales, "scales", (torch.float16,))
+    _check(x, "x", tuple(_ACT_DT))
+    _check(sign_bits, "sign_bits", (torch.int32,))
+    b, k = x.shape
+    n = packed.shape[0]
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _check(y, "y", (torch.float32,))
+    _call("tb_linear", _packing(packing), _ptr(packed), _ptr(scales), _ptr(x), _ACT_DT[x.dtype],
+          _ptr(sign_bits), _ptr(y), b, n, k, _stream(stream))
     return y
 
 

@@ -190,6 +190,106 @@ __device__ __forceinline__ void load_x(const void* __restrict__ xr, int k, int b
   }
 }
 
+// ---------------------------------------------------------------- fused rotation
+//
+// With the rotation fused (tb_linear), a prep wave rotates whole (batch,
+// 1024-block) units: x' = H_1024 (S x) / 32 ("Ternary Bonsai 2 27B release",
+// section "How the ternary weights reach 1.76 bit"), as a Sylvester-ordered
+// fast Walsh-Hadamard transform ("TensorSharp view of Ternary Bonsai 2 27B",
+// sections 3.2 and 5.2): index bits 0..3 in registers (16 consecutive
+// values per lane), bits 4..7 in registers after a transpose through the
+// wave's LDS scratch, bits 8..9 across lanes.  The result stays in the
+// scratch (element i at i + i/16, padded against bank conflicts) for the
+// limb teams.
+constexpr int kRotScratch = 1088 * 4;  // bytes of one wave's scratch
+constexpr int kMaxRotWaves = 8;
+
+template <int DT>
+__device__ __forceinline__ void load16_x(const void* base, int64_t off, float (&v)[16]) {
+  if constexpr (DT == 0) {  // fp32
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = p[q];
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 u = p[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = w[e] & 0xFFFFu, hi = w[e] >> 16;
+        if constexpr (DT == 2) {  // bf16: the upper half of an fp32
+          v[8 * q + 2 * e] = __uint_as_float(lo << 16);
+          v[8 * q + 2 * e + 1] = __uint_as_float(hi << 16);
+        } else {  // fp16
+          v[8 * q + 2 * e] = float(__builtin_bit_cast(_Float16, uint16_t(lo)));
+          v[8 * q + 2 * e + 1] = float(__builtin_bit_cast(_Float16, uint16_t(hi)));
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void butterfly16(float (&v)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      const float a = v[j], c = v[j + h];
+      v[j] = a + c;
+      v[j + h] = a - c;
+    }
+}
+
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Rotate one block held as 16 values per lane (lane l: elements 16l..16l+15,
+// sign flip already applied) into the wave's scratch L.
+__device__ __forceinline__ void rotate_block(float (&v)[16], float* L, int lane) {
+  butterfly16(v);  // index bits 0..3
+#pragma unroll
+  for (int j = 0; j < 16; ++j) L[17 * lane + j] = v[j];
+  wave_fence();
+  const int bidx = (lane & 15) + 272 * (lane >> 4);  // element (lane & 15) + 16 j + 256 (lane >> 4)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = L[bidx + 17 * j];
+  butterfly16(v);  // index bits 4..7
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1)  // index bits 8, 9 = lane bits 4, 5
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float o = __shfl_xor(v[j], m, 64);
+      v[j] = (lane & m) ? (o - v[j]) : (v[j] + o);
+    }
+  wave_fence();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) L[bidx + 17 * j] = v[j] * 0.03125f;
+  wave_fence();
+}
+
+// A thread's elements of group gi (0..7) of the rotated block in L, in the
+// same assignment as load_x.
+template <int PACK>
+__device__ __forceinline__ void load_x_rot(const float* L, int gi, int l16, float (&x)[10]) {
+  const int first = XMap<PACK>::first(l16);
+#pragma unroll
+  for (int e = 0; e < 10; ++e) {
+    const int t = first + e;
+    const int i = gi * kGroup + min(t, kGroup - 1);
+    const float v = L[i + (i >> 4)];
+    x[e] = (e < XMap<PACK>::kElems && t < kGroup) ? v : 0.f;
+  }
+}
+
 // Butterfly reductions over the 16 lanes of a DPP row (a team), no LDS.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -567,10 +667,14 @@ __device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, uin
 // launches on one stream run in order).  A workgroup holds rt row tiles of
 // 16 rows; the stages of a tile are split over ks waves, and the ks partial
 // sums are added through LDS at the end.
-template <int PACK, int NR, int XDT, bool ALIGNED>
+// ROT: xr is the unrotated x (dtype XDT: fp32, fp16, bf16) and the prep waves
+// rotate it (g_begin and ng are then multiples of 8 groups = whole blocks);
+// otherwise xr is x' (XDT: fp32, fp16).
+template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, const void* __restrict__ xr,
-    float* __restrict__ y, int nb, int n, int k, int g_begin, int ng, int accumulate, int rt, int ks) {
+    const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int nb, int n, int k, int g_begin, int ng,
+    int accumulate, int rt, int ks) {
   using F = Fmt<PACK>;
   extern __shared__ __align__(16) uint8_t smem[];
   // the wave index through readfirstlane: per-wave quantities below become
@@ -612,11 +716,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   // another wave's weight loads to be issued.
   const int pairs = ng * nb;
   const int nwaves = rt * ks;
-  const int prep_waves = min(nwaves, (pairs + 11) / 12);  // ~3 (batch, group) pairs per team
+  // rotation units: (batch, block) pairs, one wave each at a time
+  const int nblk = ng / 8, units = nb * nblk;
+  const int prep_waves = ROT ? min(min(nwaves, units), kMaxRotWaves)
+                             : min(nwaves, (pairs + 11) / 12);  // ~3 (batch, group) pairs per team
   const bool prep = wave < prep_waves;
   const int team = tid / kTeam, l16 = tid % kTeam, nteams = prep_waves * (64 / kTeam);
   float xa[10], xb[10], xc[10];
-  if (prep) {
+  float va[16];
+  if constexpr (ROT) {
+    if (prep) {
+      // the first unit's activations go out before any weight load
+      const int b = wave % nb, blk = wave / nb;
+      load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
+    }
+  } else if (prep) {
     // the activation loads go out before any weight load of the workgroup
     // (loads return in order, so whatever is issued behind the weight stream
     // arrives after it)
@@ -657,13 +771,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
         for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
       }
     }
-    const int p0 = team, p1 = team + nteams, p2 = team + 2 * nteams;
-    if (p0 < pairs) limbs_for_group<PACK>(sm, p0 % nb, p0 / nb, l16, xa);
-    if (p1 < pairs) limbs_for_group<PACK>(sm, p1 % nb, p1 / nb, l16, xb);
-    if (p2 < pairs) limbs_for_group<PACK>(sm, p2 % nb, p2 / nb, l16, xc);
-    for (int pr = team + 3 * nteams; pr < pairs; pr += nteams) {
-      load_x<XDT, PACK>(xr, k, pr % nb, g_begin + pr / nb, l16, xa);
-      limbs_for_group<PACK>(sm, pr % nb, pr / nb, l16, xa);
+    if constexpr (ROT) {
+      // units wave, wave + prep_waves, ...: sign flip, rotate into this wave's
+      // scratch (inside the staging region, unused until matrix work starts),
+      // then four teams make the limbs of the block's 8 groups
+      float* L = reinterpret_cast<float*>(sm.stage + wave * kRotScratch);
+      const int tw = lane >> 4;
+      for (int u = wave; u < units; u += prep_waves) {
+        const int b = u % nb, blk = u / nb;
+        if (u != wave)
+          load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
+        const int beta = (g_begin >> 3) + blk;  // block index in the row
+        const uint32_t sw = sign_bits[beta * 32 + (lane >> 1)] >> ((lane & 1) * 16);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) va[j] = __uint_as_float(__float_as_uint(va[j]) ^ (((sw >> j) & 1u) << 31));
+        rotate_block(va, L, lane);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int gi = tw + 4 * h;
+          float xg[10];
+          load_x_rot<PACK>(L, gi, l16, xg);
+          limbs_for_group<PACK>(sm, b, 8 * blk + gi, l16, xg);
+        }
+        wave_fence();  // the scratch is rewritten by the next unit
+      }
+    } else {
+      const int p0 = team, p1 = team + nteams, p2 = team + 2 * nteams;
+      if (p0 < pairs) limbs_for_group<PACK>(sm, p0 % nb, p0 / nb, l16, xa);
+      if (p1 < pairs) limbs_for_group<PACK>(sm, p1 % nb, p1 / nb, l16, xb);
+      if (p2 < pairs) limbs_for_group<PACK>(sm, p2 % nb, p2 / nb, l16, xc);
+      for (int pr = team + 3 * nteams; pr < pairs; pr += nteams) {
+        load_x<XDT, PACK>(xr, k, pr % nb, g_begin + pr / nb, l16, xa);
+        limbs_for_group<PACK>(sm, pr % nb, pr / nb, l16, xa);
+      }
     }
     // this wave's LDS writes complete before its count is seen
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -746,7 +886,17 @@ struct Plan {
   int rt, ks, ng;
 };
 
+// LDS beyond the staging region that the fused rotation's scratch needs
+// (prep waves borrow the staging buffers, which are free until the matrix
+// work starts).
 template <int PACK>
+constexpr int rot_extra(int nwaves, int units) {
+  const int p = nwaves < units ? nwaves : units;
+  const int need = (p < kMaxRotWaves ? p : kMaxRotWaves) * kRotScratch - nwaves * Fmt<PACK>::kStageLds;
+  return need > 0 ? (need + 15) / 16 * 16 : 0;
+}
+
+template <int PACK, bool ROT>
 Plan make_plan(int b, int n, int k) {
   using F = Fmt<PACK>;
   const int tiles = (n + 15) / 16;
@@ -760,7 +910,8 @@ Plan make_plan(int b, int n, int k) {
   // At one wave per tile the room is always enough for >= 8 groups (batch <= 8).
   int ks = kMaxWaves / rt, ng = 0;
   for (; ks >= 1; --ks) {
-    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 127 - 31;
+    const int extra = ROT ? rot_extra<PACK>(rt * ks, 1 << 20) : 0;
+    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 127 - 31 - extra;
     ng = room > 0 ? room / per_group : 0;
     if (ng >= kStageGroups || ks == 1) break;
   }
@@ -772,16 +923,16 @@ Plan make_plan(int b, int n, int k) {
   return Plan{rt, ks, ng};
 }
 
-template <int PACK, int NR, int XDT, bool ALIGNED>
-void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, float* y, int b, int n, int k,
-                hipStream_t s) {
+template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
+void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, const uint32_t* sign_bits, float* y,
+                int b, int n, int k, hipStream_t s) {
   using F = Fmt<PACK>;
   const int groups = k / kGroup;
-  const Plan pl = make_plan<PACK>(b, n, k);
+  const Plan pl = make_plan<PACK, ROT>(b, n, k);
   if (pl.ng < 1) return;  // unreachable for batch <= 8 (see make_plan); never loop without progress
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_kernel<PACK, NR, XDT, ALIGNED>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   });
   const int tiles = (n + 15) / 16;
@@ -790,17 +941,19 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, f
     const int ng = groups - g0 < pl.ng ? groups - g0 : pl.ng;
     const int nst = (ng + kStageGroups - 1) / kStageGroups;
     const int ks = pl.ks < nst ? pl.ks : nst;
-    const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) + pl.rt * ks * F::kStageLds;
-    gemv_mfma_kernel<PACK, NR, XDT, ALIGNED><<<grid, 64 * pl.rt * ks, lds, s>>>(
-        packed, scales, xr, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks);
+    const int extra = ROT ? rot_extra<PACK>(pl.rt * ks, b * (ng / 8)) : 0;
+    const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) +
+                    pl.rt * ks * F::kStageLds + extra;
+    gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT><<<grid, 64 * pl.rt * ks, lds, s>>>(
+        packed, scales, xr, sign_bits, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks);
   }
 }
 
 template <int PACK, int NR, int XDT>
 void launch_a(const uint8_t* p, const uint16_t* sc, const void* xr, float* y, int b, int n, int k, hipStream_t s) {
   // 16-byte scale loads need every row's scales 16-byte aligned: K % 1024 == 0
-  if ((k / kGroup) % 8 == 0) launch_one<PACK, NR, XDT, true>(p, sc, xr, y, b, n, k, s);
-  else launch_one<PACK, NR, XDT, false>(p, sc, xr, y, b, n, k, s);
+  if ((k / kGroup) % 8 == 0) launch_one<PACK, NR, XDT, true, false>(p, sc, xr, nullptr, y, b, n, k, s);
+  else launch_one<PACK, NR, XDT, false, false>(p, sc, xr, nullptr, y, b, n, k, s);
 }
 
 template <int PACK, int NR>
@@ -808,6 +961,15 @@ void launch_x(const uint8_t* p, const uint16_t* sc, const void* xr, int xdt, flo
               hipStream_t s) {
   if (xdt == 0) launch_a<PACK, NR, 0>(p, sc, xr, y, b, n, k, s);
   else launch_a<PACK, NR, 1>(p, sc, xr, y, b, n, k, s);
+}
+
+template <int PACK, int NR>
+void launch_rot(const uint8_t* p, const uint16_t* sc, const void* x, int xdt, const uint32_t* sb, float* y, int b,
+                int n, int k, hipStream_t s) {
+  // K % 1024 == 0 here, so the scales are always 16-byte aligned per row
+  if (xdt == 0) launch_one<PACK, NR, 0, true, true>(p, sc, x, sb, y, b, n, k, s);
+  else if (xdt == 1) launch_one<PACK, NR, 1, true, true>(p, sc, x, sb, y, b, n, k, s);
+  else launch_one<PACK, NR, 2, true, true>(p, sc, x, sb, y, b, n, k, s);
 }
 
 }  // namespace
@@ -820,6 +982,17 @@ void launch_gemv(int packing, const uint8_t* packed, const uint16_t* scales, con
   } else {
     if (b <= 4) launch_x<1, 1>(packed, scales, xr, xr_dt, y, b, n, k, s);
     else launch_x<1, 2>(packed, scales, xr, xr_dt, y, b, n, k, s);
+  }
+}
+
+void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
+                   const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s) {
+  if (packing == 0) {
+    if (b <= 4) launch_rot<0, 1>(packed, scales, x, x_dt, sign_bits, y, b, n, k, s);
+    else launch_rot<0, 2>(packed, scales, x, x_dt, sign_bits, y, b, n, k, s);
+  } else {
+    if (b <= 4) launch_rot<1, 1>(packed, scales, x, x_dt, sign_bits, y, b, n, k, s);
+    else launch_rot<1, 2>(packed, scales, x, x_dt, sign_bits, y, b, n, k, s);
   }
 }
 

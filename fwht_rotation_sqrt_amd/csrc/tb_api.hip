@@ -97,6 +97,21 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
   return finish_launch();
 }
 
+int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+              const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream) {
+  if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
+  if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(N, K) || !fits(B, K))
+    return TB_ERR_SHAPE;
+  if (x_dtype != TB_F32 && x_dtype != TB_F16 && x_dtype != TB_BF16) return TB_ERR_DTYPE;
+  if (N == 0) return TB_OK;
+  if (!packed || !scales || !x || !sign_bits || !y) return TB_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y))
+    return TB_ERR_ALIGN;
+  tb::launch_linear(packing, packed, scales, x, x_dtype, sign_bits, y, int(B), int(N), int(K),
+                    static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (packing != TB_PACK_2BIT) return TB_ERR_UNSUPPORTED;

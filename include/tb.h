@@ -112,6 +112,21 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
 int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
             int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, void* stream);
 
+/* The whole linear at decode, y[b][n] = sum_k W_hat[n][k] (R_K x[b])[k], in one
+ * launch: the rotation of x is done inside the product's prologue instead of
+ * by a separate tb_fwht_rotate call.
+ * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
+ * reach 1.76 bit" (f(x) = W(Rx) with R = H_1024 S / 32 blockwise) and "Known
+ * weaknesses" (at batch 1 the activation transform is the largest cost
+ * besides the product).
+ * x: [B][K] unrotated activations of x_dtype (TB_F32, TB_F16 or TB_BF16);
+ * sign_bits, packed, scales and y as for tb_fwht_rotate and tb_gemv.
+ * K % 1024 == 0; 1 <= B <= TB_GEMV_MAX_BATCH.  x' is kept in fp32 inside the
+ * call (never rounded to fp16), so the result matches tb_fwht_rotate to fp32
+ * followed by tb_gemv to fp32 accumulation order. */
+int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+              const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream);
+
 /* Prefill product Y = X' W_hat^T for many rows: Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k].
  * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
  * reach 1.76 bit" and "Throughput" (pp512 prompt processing).

@@ -95,6 +95,26 @@ def test_gemv_validation():
     assert g(1, P, P, P, 0, P, 1, 1 << 20, 1 << 12, None) == SHAPE   # > 2^31 weights
 
 
+def test_linear_validation():
+    lib = tb.library()
+    g = lib.tb_linear
+    # (packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream)
+    assert g(3, P, P, P, 2, P, P, 1, 8, 1024, None) == UNSUP
+    assert g(1, P, P, P, 2, P, P, 0, 8, 1024, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, 9, 8, 1024, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, 1, 8, 1152, None) == SHAPE      # K % 1024 != 0
+    assert g(1, P, P, P, 2, P, P, 1, -8, 1024, None) == SHAPE
+    assert g(1, P, P, P, 3, P, P, 1, 8, 1024, None) == DTYPE
+    assert g(1, P, P, P, 2, None, P, 1, 8, 1024, None) == NULL    # sign bits
+    assert g(1, None, P, P, 2, P, P, 1, 8, 1024, None) == NULL
+    assert g(1, P, P, None, 2, P, P, 1, 8, 1024, None) == NULL
+    assert g(1, P, P, P, 2, P, None, 1, 8, 1024, None) == NULL
+    assert g(1, P, P, P, 2, MIS, P, 1, 8, 1024, None) == ALIGN
+    assert g(0, P, P, MIS, 0, P, P, 1, 8, 1024, None) == ALIGN
+    assert g(0, P, P, P, 1, P, P, 1, 0, 1024, None) == OK         # empty
+    assert g(0, P, P, P, 0, P, P, 1, 1 << 20, 1 << 12, None) == SHAPE
+
+
 def test_gemm_validation():
     lib = tb.library()
     g = lib.tb_gemm

@@ -159,6 +159,11 @@ def _e2e_gemv(wid, packing, n, k, x_dtype, outliers, batches, layer=0, linear=0)
         y = host(tb.tb_gemv(packing, packed, sd, xr))
         errs[b] = oracle.rel_err(y, want[:b])
         assert errs[b] < TOL, (b, errs[b])
+        if k % 1024 == 0:
+            # the same linear with the rotation inside the product
+            y1 = host(tb.tb_linear(packing, packed, sd, xd[:b].contiguous(), sgn))
+            e1 = oracle.rel_err(y1, want[:b])
+            assert e1 < TOL, ("tb_linear", b, e1)
     return errs
 
 
@@ -178,6 +183,33 @@ def test_block_linears_b1_b8(packing, li):
     lin = synth.BLOCK_LINEARS[li]
     note(f"block linear {lin.name} {lin.n}x{lin.k} {packing} batch 1 and 8")
     _e2e_gemv(2, packing, lin.n, lin.k, "bf16", False, (1, 8), 0, li)
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("n,k", [(1, 1024), (16, 1024), (37, 2048), (300, 3072), (1000, 5120), (81, 17408)])
+@pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
+def test_linear_fused_rotation(packing, n, k, x_dtype):
+    note(f"tb_linear {packing} n={n} k={k} x={x_dtype}")
+    g = synth.rng(240, 0, n % 251, k // 1024)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x32 = g.standard_normal((8, k)).astype(np.float32)
+    if x_dtype == "bf16":
+        xbits = synth.f32_to_bf16_bits(x32)
+        x64, xd = synth.bf16_bits_to_f64(xbits), act_dev(xbits, "bf16")
+    elif x_dtype == "f16":
+        x16 = x32.astype(np.float16)
+        x64, xd = x16.astype(np.float64), dev(x16)
+    else:
+        x64, xd = x32.astype(np.float64), dev(x32)
+    packed, _ = PACK_REF[packing](t)
+    want = oracle.gemv(packing, packed, s, oracle.rotate(x64, signs), k)
+    pd, sd, sgn = dev(packed), scales_dev(s), signs_dev(signs)
+    for b in (1, 3, 5, 8):
+        got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
+        assert got.shape == (b, n)
+        assert oracle.rel_err(got, want[:b]) < TOL, b
 
 
 # ------------------------------------------------------------------ prefill product
