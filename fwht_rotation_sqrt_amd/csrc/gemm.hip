@@ -15,14 +15,19 @@
 //   * X' (A): the 128 x 128 fp16 tile is staged through registers into one of
 //     two LDS buffers (rows padded to 272 bytes) while the previous K-step
 //     computes.
-//   * W (B): never stored as fp16.  Each lane loads the 8 code bytes it needs
-//     (one row, 32 codes) straight from global memory; per 8 codes it makes
-//     two LDS table lookups (byte -> four fp16 trits {-1, 0, +1}) and two
-//     packed fp16 multiplies by the group's scale, which are exact.
+//   * W (B): never stored as fp16.  The tile's 272 rows x 32 code bytes of a
+//     group are loaded once per workgroup (two threads per row, coalesced)
+//     and staged in LDS, as are the scales, 8 groups at a time; a load
+//     instruction that served one wave's 16 rows instead would touch 16
+//     cache lines for 32 bytes each, and the other waves would repeat it.
+//     Each lane reads its 8 code bytes and its scale one K-step ahead; per 8
+//     codes it makes two LDS table lookups (byte -> four fp16 trits
+//     {-1, 0, +1}) and two packed fp16 multiplies by the scale, which are
+//     exact.
 //   * K order: inside a group, instruction chunk kc (32 K-slots) takes, from
 //     lane group q, the eight codes 32q + 8kc .. 32q + 8kc + 7.  Slot order is
 //     free as long as both operands agree, and this one gives every lane a
-//     contiguous 8-byte code load and a contiguous 16-byte A read.
+//     contiguous 8-byte code read and a contiguous 16-byte A read.
 // The workgroup-to-tile map keeps the M-tiles that share a weight slab on one
 // XCD (workgroups are handed to the 8 XCDs round robin), so the slab is read
 // from HBM once per XCD L2.
@@ -43,7 +48,14 @@ constexpr int kTileN = 16 * kNBlocks;         // 272
 constexpr int kARowLds = 2 * kGroup + 16;     // 272 bytes: 128 fp16 + pad (16 lanes of a read in distinct banks)
 constexpr int kABuf = kTileM * kARowLds;      // 34816 bytes per A buffer
 constexpr int kTableBytes = 256 * 256;        // entry e at 256 e, copy c (lane & 31) at + 8 c
-constexpr int kLds = kTableBytes + 2 * kABuf; // 135168
+constexpr int kCodeRow = kGroup / 4;          // 32 code bytes per row and group
+constexpr int kCBuf = kTileN * kCodeRow;      // 8704 bytes per code buffer
+constexpr int kSChunk = 8;                    // groups per staged scale chunk
+constexpr int kSBuf = kTileN * kSChunk * 2;   // 4352 bytes per scale buffer
+constexpr int kAOff = kTableBytes;            // two A buffers
+constexpr int kCOff = kAOff + 2 * kABuf;      // two code buffers
+constexpr int kSOff = kCOff + 2 * kCBuf;      // two scale buffers
+constexpr int kLds = kSOff + 2 * kSBuf;       // 161280 of the 163840 a workgroup may hold
 constexpr uint32_t kNoLoad = 0x80000000u;     // buffer offset past any buffer: reads zero
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -74,10 +86,10 @@ __device__ __forceinline__ u32x2 trit_halves(uint32_t byte) {
   return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
-// Per-lane state of one of the wave's five decoded column blocks.
+// Per-lane B inputs of one K-step in one of the wave's five column blocks.
 struct ColBlock {
-  u32x2 codes;     // this lane's 32 codes (8 bytes) of the current group
-  uint32_t s2;     // the group's fp16 scale, twice
+  u32x2 codes;     // this lane's 32 codes (8 bytes) of the group
+  uint32_t s;      // the group's fp16 scale (low half)
 };
 
 // Operands of one chunk (32 K-slots) in flight: the wave's four A rows and
@@ -120,40 +132,47 @@ __device__ __forceinline__ half8 b_operand(const u32x2 (&t)[2], uint32_t s2) {
 }
 
 // The 17 matrix instructions of one fetched chunk.
-__device__ __forceinline__ void chunk_mma(const ChunkRaw& r, const ColBlock (&cb)[5], floatx4 (&acc)[4][4],
+__device__ __forceinline__ void chunk_mma(const ChunkRaw& r, const uint32_t (&s2)[5], floatx4 (&acc)[4][4],
                                           floatx4& acc16) {
   half8 a[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) a[mb] = __builtin_bit_cast(half8, r.a[mb]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const half8 b = b_operand(r.t[j], cb[j].s2);
+    const half8 b = b_operand(r.t[j], s2[j]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
       acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], b, acc[mb][j], 0, 0, 0);
   }
-  acc16 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b_operand(r.t[4], cb[4].s2), acc16, 0, 0, 0);
+  acc16 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b_operand(r.t[4], s2[4]), acc16, 0, 0, 0);
 }
 
 // One K-step (one 128-group): chunk kc+1's LDS reads are issued before chunk
-// kc's matrix instructions, so their latency hides behind them.
+// kc's matrix instructions, so their latency hides behind them.  `ahead`
+// issues the reads of the next K-step's codes and scales, after this step's
+// own reads.
+template <typename Ahead>
 __device__ __forceinline__ void k_step(const uint32_t (&a_addr)[4], uint32_t buf, const ColBlock (&cb)[5],
-                                       uint32_t tab, floatx4 (&acc)[4][4], floatx4& acc16) {
+                                       uint32_t tab, floatx4 (&acc)[4][4], floatx4& acc16, Ahead&& ahead) {
+  uint32_t s2[5];
+#pragma unroll
+  for (int c = 0; c < 5; ++c) s2[c] = cb[c].s * 0x10001u;
   ChunkRaw r0, r1;
   fetch<0>(a_addr, buf, cb, tab, r0);
   fetch<1>(a_addr, buf, cb, tab, r1);
   __builtin_amdgcn_sched_barrier(0);
-  chunk_mma(r0, cb, acc, acc16);
+  chunk_mma(r0, s2, acc, acc16);
   __builtin_amdgcn_sched_barrier(0);
   fetch<2>(a_addr, buf, cb, tab, r0);
   __builtin_amdgcn_sched_barrier(0);
-  chunk_mma(r1, cb, acc, acc16);
+  chunk_mma(r1, s2, acc, acc16);
   __builtin_amdgcn_sched_barrier(0);
   fetch<3>(a_addr, buf, cb, tab, r1);
+  ahead();
   __builtin_amdgcn_sched_barrier(0);
-  chunk_mma(r0, cb, acc, acc16);
+  chunk_mma(r0, s2, acc, acc16);
   __builtin_amdgcn_sched_barrier(0);
-  chunk_mma(r1, cb, acc, acc16);
+  chunk_mma(r1, s2, acc, acc16);
 }
 
 __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __restrict__ packed,
@@ -180,49 +199,103 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xr, uint32_t(m) * uint32_t(k) * 2u);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, uint32_t(n) * uint32_t(k / 4));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(scales, uint32_t(n) * uint32_t(groups) * 2u);
-  // A staging: thread -> (row tid / 4, quarter tid % 4 of the 256-byte group row)
-  const int arow = tid >> 2, aq = tid & 3;
-  const uint32_t a_src = m0 + arow < m ? uint32_t((m0 + arow) * k * 2 + aq * 64) : kNoLoad;
-  const uint32_t a_dst = uint32_t(kTableBytes + arow * kARowLds + aq * 64);
-  // B: the lane's row in each of its five column blocks
-  uint32_t w_src[5], s_src[5];
+  // A staging: load i takes rows 32 i .. 32 i + 31, sixteen threads per
+  // 256-byte group row (a wave reads 4 whole rows, 8 full cache lines)
+  const int arow = tid >> 4, apiece = tid & 15;
+  uint32_t a_src[4];
 #pragma unroll
-  for (int c = 0; c < 5; ++c) {
-    const int row = n0 + 16 * (c < 4 ? 4 * wn + c : 16) + nl;
-    w_src[c] = row < n ? uint32_t(row * (k / 4) + 8 * q) : kNoLoad;
-    s_src[c] = row < n ? uint32_t(row * groups * 2) : kNoLoad;
+  for (int i = 0; i < 4; ++i)
+    a_src[i] = m0 + arow + 32 * i < m ? uint32_t((m0 + arow + 32 * i) * k * 2 + apiece * 16) : kNoLoad;
+  const uint32_t a_dst = uint32_t(kAOff + arow * kARowLds + apiece * 16);
+  // code staging: 16-byte piece p = row p / 2, half p % 2 of the tile's
+  // 272 x 32-byte slab of one group; thread tid takes piece tid, and the
+  // first 32 threads also piece 512 + tid (rows 256..271)
+  constexpr int kPieces2 = 2 * kTileN - 64 * kWaves;   // 32
+  const bool two_pieces = tid < kPieces2;
+  uint32_t c_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pc = tid + 64 * kWaves * i, row = n0 + (pc >> 1);
+    c_src[i] = (i == 0 || two_pieces) && row < n ? uint32_t(row * (k / 4) + 16 * (pc & 1)) : kNoLoad;
   }
+  const uint32_t c_dst = uint32_t(kCOff + tid * 16);   // piece p sits at 16 p
+  // scale staging: element e = tid + 512 i of a 272 x 8 chunk: row e / 8,
+  // group 8 chunk + e % 8 (eight threads read a row's 16 contiguous bytes)
+  constexpr int kSElems = kTileN * kSChunk;             // 2176
+  const int sj = tid & 7;
+  const uint32_t s_dst = uint32_t(kSOff + tid * 2);     // element e sits at 2 e
+  // per-lane reads: row nl of each column block, code bytes 8q .. 8q + 7
+  const uint32_t code_rd = uint32_t(kCOff + (64 * wn + nl) * kCodeRow + 8 * q);
+  const uint32_t code_rd16 = uint32_t(kCOff + (256 + nl) * kCodeRow + 8 * q);
+  const uint32_t scale_rd = uint32_t(kSOff + (64 * wn + nl) * kSChunk * 2);
+  const uint32_t scale_rd16 = uint32_t(kSOff + (256 + nl) * kSChunk * 2);
   const uint32_t tab = uint32_t(8 * (lane & 31));
   // A operand read: row nl of each M-block (rotated order), K-slots 32q + 8kc .. of the group
   uint32_t a_addr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    a_addr[i] = uint32_t(kTableBytes + (16 * (4 * wm + ((i + wn) & 3)) + nl) * kARowLds + 64 * q);
+    a_addr[i] = uint32_t(kAOff + (16 * (4 * wm + ((i + wn) & 3)) + nl) * kARowLds + 64 * q);
 
+  // Loads of a group past the end read zeros (offset outside the buffer).
   auto load_a = [&](int g, u32x4 (&ra)[4]) {
+    const bool live = g < groups;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, a_src == kNoLoad ? kNoLoad : a_src + g * 256 + 16 * i, 0, 0);
-  };
-  auto load_b = [&](int g, ColBlock (&cb)[5]) {
-#pragma unroll
-    for (int c = 0; c < 5; ++c) {
-      cb[c].codes = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, w_src[c] == kNoLoad ? kNoLoad : w_src[c] + 32 * g, 0, 0));
-      const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(srs, s_src[c] == kNoLoad ? kNoLoad : s_src[c] + 2 * g, 0, 0);
-      cb[c].s2 = s | (s << 16);
-    }
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, a_src[i] == kNoLoad || !live ? kNoLoad : a_src[i] + g * 256,
+                                                    0, 0);
   };
   auto store_a = [&](int buf, const u32x4 (&ra)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_write<u32x4>(a_dst + buf * kABuf + 16 * i, ra[i]);
+    for (int i = 0; i < 4; ++i) lds_write<u32x4>(a_dst + buf * kABuf + 32 * kARowLds * i, ra[i]);
+  };
+  auto load_codes = [&](int g, u32x4 (&rc)[2]) {
+    const bool live = g < groups;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rc[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          wrs, c_src[i] == kNoLoad || !live ? kNoLoad : c_src[i] + g * kCodeRow, 0, 0);
+  };
+  auto store_codes = [&](int buf, const u32x4 (&rc)[2]) {
+    lds_write<u32x4>(c_dst + buf * kCBuf, rc[0]);
+    if (two_pieces) lds_write<u32x4>(c_dst + buf * kCBuf + 64 * kWaves * 16, rc[1]);
+  };
+  auto load_scales = [&](int chunk, uint32_t (&rs)[5]) {
+    const bool live = kSChunk * chunk + sj < groups;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int e = tid + 64 * kWaves * i, row = n0 + (e >> 3);
+      rs[i] = __builtin_amdgcn_raw_buffer_load_b16(
+          srs, live && e < kSElems && row < n ? uint32_t((row * groups + kSChunk * chunk + sj) * 2) : kNoLoad, 0, 0);
+    }
+  };
+  auto store_scales = [&](int buf, const uint32_t (&rs)[5]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_write<uint16_t>(s_dst + buf * kSBuf + 64 * kWaves * 2 * i, uint16_t(rs[i]));
+    if (tid + 64 * kWaves * 4 < kSElems) lds_write<uint16_t>(s_dst + buf * kSBuf + 64 * kWaves * 2 * 4, uint16_t(rs[4]));
+  };
+  // this lane's codes and scales of K-step g (code buffer g % 2, scale
+  // buffer (g / 8) % 2)
+  auto read_b = [&](int g, ColBlock (&cb)[5]) {
+    const uint32_t cbuf = uint32_t(g & 1) * kCBuf;
+    const uint32_t sbuf = uint32_t((g / kSChunk) & 1) * kSBuf + uint32_t(g % kSChunk) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      cb[c].codes = lds_read<u32x2>(code_rd + cbuf + c * 16 * kCodeRow);
+      cb[c].s = lds_read<uint16_t>(scale_rd + sbuf + c * 16 * kSChunk * 2);
+    }
+    cb[4].codes = lds_read<u32x2>(code_rd16 + cbuf);
+    cb[4].s = lds_read<uint16_t>(scale_rd16 + sbuf);
   };
 
-  // ---- prologue: first loads, then the table while they fly
-  u32x4 ra[4];
-  ColBlock cur[5], nxt[5];
+  // ---- prologue: first loads, then the table while they fly.  K-step g
+  // takes A from buffer g % 2 (staged at the end of step g - 1), its codes
+  // and scales from registers read at the top of step g - 1; even steps keep
+  // them in bA, odd ones in bB.
+  u32x4 ra[4], rc[2];
+  uint32_t rs[5];
+  load_scales(0, rs);
   load_a(0, ra);
-  load_b(0, cur);
+  load_codes(0, rc);
   {
     // table: thread -> entry tid / 2, half of its 32 copies
     const u32x2 v = trit_halves(uint32_t(tid >> 1));
@@ -231,11 +304,17 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
 #pragma unroll
     for (int i = 0; i < 8; ++i) lds_write<u32x4>(uint32_t(256 * (tid >> 1) + 128 * (tid & 1) + 16 * i), v2);
   }
+  store_scales(0, rs);
   store_a(0, ra);
-  if (groups > 1) {
-    load_a(1, ra);
-    load_b(1, nxt);
-  }
+  store_codes(0, rc);
+  load_a(1, ra);
+  load_codes(1, rc);
+  store_codes(1, rc);
+  load_codes(2, rc);
+  __syncthreads();
+  ColBlock bA[5], bB[5];
+  read_b(0, bA);
+  // step 0 rewrites code buffer 0: every wave's reads of it come first
   __syncthreads();
 
   floatx4 acc[4][4], acc16;
@@ -245,21 +324,30 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
     for (int c = 0; c < 4; ++c) acc[mb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
   acc16 = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = 0; g < groups; ++g) {
-    k_step(a_addr, uint32_t((g & 1) * kABuf), cur, tab, acc, acc16);
-    if (g + 1 < groups) {
-      // stage K-step g+1 (its buffer was last read in iteration g-1, before
-      // the previous barrier), then start the loads of K-step g+2
-      store_a((g + 1) & 1, ra);
-#pragma unroll
-      for (int c = 0; c < 5; ++c) cur[c] = nxt[c];
-      if (g + 2 < groups) {
-        load_a(g + 2, ra);
-        load_b(g + 2, nxt);
-      }
-    }
-    __syncthreads();
+  // Step g, p = g % 2.  After its matrix work it stages A of step g + 1
+  // (buffer p ^ 1, last read in step g - 1), codes of step g + 2 (code
+  // buffer p, last read at the top of step g - 1) and, every 8 steps, the
+  // next scale chunk, then starts the loads for later steps.  The barrier
+  // orders LDS traffic only: the loads in flight target registers, so it
+  // waits for the LDS counter, not the memory one.
+  auto step = [&](int g, uint32_t p, const ColBlock (&cb)[5], ColBlock (&nb)[5]) {
+    k_step(a_addr, p * uint32_t(kABuf), cb, tab, acc, acc16, [&] { read_b(g + 1, nb); });
+    store_a(int(p ^ 1u), ra);
+    store_codes(int(p), rc);
+    if (((g + 2) % kSChunk) == 0) store_scales(((g + 2) / kSChunk) & 1, rs);
+    load_a(g + 2, ra);
+    load_codes(g + 3, rc);
+    if (((g + 3) % kSChunk) == 0) load_scales((g + 3) / kSChunk, rs);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  int g = 0;
+  for (; g + 1 < groups; g += 2) {
+    step(g, 0u, bA, bB);
+    step(g + 1, 1u, bB, bA);
   }
+  if (g < groups) step(g, 0u, bA, bB);
 
   // ---- store: lane holds rows 4q..4q+3 of column nl of each block
 #pragma unroll
