@@ -12,8 +12,9 @@ consecutive steps never hit the 256 MB Infinity Cache; step i uses copy
 i mod copies.  The K timed steps are captured in one HIP graph and replayed.
 
 Also measured, in the same run: the pp512 prefill product (M=512, N=17408,
-K=5120, 2-bit codes; rotate to fp16 then tb_gemm) in TFLOP/s, the rotation
-alone, and the oracle on the host cores as a baseline.
+K=5120; rotate to fp16 then tb_gemm) in TFLOP/s for 2-bit codes and for
+base-3 bytes, the rotation alone, and the oracle on the host cores as a
+baseline.
 
 Prints one JSON line (rank 0).  `value` is the decode step's packed-weight
 stream rate in GB/s (codes + scales per step / step time).
@@ -161,10 +162,10 @@ def bench_decode(d, steps, warmup):
     return wall, t_fused, t_gemv, t_rot
 
 
-def bench_gemm(steps):
+def bench_gemm(steps, packing="2bit"):
     m, n, k = 512, synth.FFN, synth.HIDDEN
     li = synth.linear_inputs(3, n, k, m, "bf16", True)
-    packed = tb.tb_pack_2bit(dev(li.trits))
+    packed = (tb.tb_pack_2bit if packing == "2bit" else tb.tb_pack_base3)(dev(li.trits))
     scales = dev(li.scales.view(np.float16))
     x = dev(li.x.view(np.int16)).view(torch.bfloat16)
     signs = dev(li.signs.view(np.int32))
@@ -174,7 +175,7 @@ def bench_gemm(steps):
 
     def gemm_only():
         for _ in range(reps):
-            tb.tb_gemm("2bit", packed, scales, xr, y=y)
+            tb.tb_gemm(packing, packed, scales, xr, y=y)
 
     def rot_only():
         for _ in range(reps):
@@ -243,6 +244,7 @@ def main():
     fused_gbs = per_copy / t_fused / 1e9
     traffic = gemv_traffic_bytes()
     gemm = None if args.no_gemm else bench_gemm(args.steps)
+    gemm3 = None if args.no_gemm else bench_gemm(args.steps, "base3")
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
     rec = {
         "metric": "packed-ternary GEMV HBM GB/s (% peak) + pp512 GEMM TFLOP/s, K=5120",
@@ -279,6 +281,9 @@ def main():
                              "frac_of_fp16_mfma_peak": round(gemm["frac"], 4), "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
                              "rotate_us_512x5120_to_f16": round(gemm["rotate_us"], 2),
                              "tokens_per_s_equiv": round(gemm["tokens_per_s"], 1)}
+    if gemm3:
+        rec["pp512_gemm_base3"] = {"tflops": round(gemm3["tflops"], 2), "us": round(gemm3["us"], 2),
+                                   "frac_of_fp16_mfma_peak": round(gemm3["frac"], 4)}
     print(json.dumps(rec), flush=True)
 
 

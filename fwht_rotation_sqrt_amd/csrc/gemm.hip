@@ -1,5 +1,5 @@
 // Prefill product Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k] on the matrix cores
-// (2-bit codes; v_mfma_f32_16x16x32_f16, fp32 accumulation).
+// (2-bit codes or base-3 bytes; v_mfma_f32_16x16x32_f16, fp32 accumulation).
 //
 // Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
 // reach 1.76 bit" (g128 fp16 scales; the unpack is part of the product) and
@@ -28,6 +28,12 @@
 //     lane group q, the eight codes 32q + 8kc .. 32q + 8kc + 7.  Slot order is
 //     free as long as both operands agree, and this one gives every lane a
 //     contiguous 8-byte code read and a contiguous 16-byte A read.
+// Base-3 weights (26 bytes per row and group, five trits per byte, least
+// significant digit first, digit = t + 1) are turned into the same 2-bit codes
+// on their way into LDS: the digits of a byte are exactly the codes of its
+// five weights, so one lookup per byte (byte -> the five codes as a 10-bit
+// field) and shifts assemble a row's 32 code bytes (the last byte's two pad
+// trits are dropped).  Everything after the code buffers is shared.
 // The workgroup-to-tile map keeps the M-tiles that share a weight slab on one
 // XCD (workgroups are handed to the 8 XCDs round robin), so the slab is read
 // from HBM once per XCD L2.
@@ -47,7 +53,10 @@ constexpr int kNBlocks = 17;                  // N-blocks of 16 per tile
 constexpr int kTileN = 16 * kNBlocks;         // 272
 constexpr int kARowLds = 2 * kGroup + 16;     // 272 bytes: 128 fp16 + pad (16 lanes of a read in distinct banks)
 constexpr int kABuf = kTileM * kARowLds;      // 34816 bytes per A buffer
-constexpr int kTableBytes = 256 * 256;        // entry e at 256 e, copy c (lane & 31) at + 8 c
+// decode table: entry e at 256 e.  2-bit codes: 32 copies of the fp16 trits,
+// copy c (lane & 31) at + 8 c.  Base-3: 16 copies of the fp16 trits at + 8 c
+// (c = lane & 15), then 32 copies of the byte's five codes at + 128 + 4 c.
+constexpr int kTableBytes = 256 * 256;
 constexpr int kCodeRow = kGroup / 4;          // 32 code bytes per row and group
 constexpr int kCBuf = kTileN * kCodeRow;      // 8704 bytes per code buffer
 constexpr int kSChunk = 8;                    // groups per staged scale chunk
@@ -84,6 +93,20 @@ __device__ __forceinline__ u32x2 trit_halves(uint32_t byte) {
     h[i] = c == 0u ? 0xBC00u : c == 2u ? 0x3C00u : 0u;
   }
   return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// The five base-3 digits of a byte (value sum d_i 3^i, d_i = t_i + 1) as a
+// 10-bit field of 2-bit codes, digit i at bits 2i..2i+1.  Bytes >= 243 are
+// invalid; they map to code 01 (zero) throughout.
+__device__ __forceinline__ uint32_t base3_codes(uint32_t byte) {
+  if (byte >= 243u) return 0x155u;
+  uint32_t f = 0, v = byte;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    f |= (v % 3u) << (2 * i);
+    v /= 3u;
+  }
+  return f;
 }
 
 // Per-lane B inputs of one K-step in one of the wave's five column blocks.
@@ -175,6 +198,7 @@ __device__ __forceinline__ void k_step(const uint32_t (&a_addr)[4], uint32_t buf
   chunk_mma(r1, s2, acc, acc16);
 }
 
+template <int PACK>
 __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __restrict__ packed,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ xr,
@@ -197,7 +221,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
 
   // ---- resources and per-lane addresses
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xr, uint32_t(m) * uint32_t(k) * 2u);
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, uint32_t(n) * uint32_t(k / 4));
+  const uint32_t row_bytes = PACK == 0 ? uint32_t(k / 4) : uint32_t(kB3GroupBytes * groups);
+  const uint32_t group_bytes = PACK == 0 ? uint32_t(kCodeRow) : uint32_t(kB3GroupBytes);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, uint32_t(n) * row_bytes);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(scales, uint32_t(n) * uint32_t(groups) * 2u);
   // A staging: load i takes rows 32 i .. 32 i + 31, sixteen threads per
   // 256-byte group row (a wave reads 4 whole rows, 8 full cache lines)
@@ -207,18 +233,27 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   for (int i = 0; i < 4; ++i)
     a_src[i] = m0 + arow + 32 * i < m ? uint32_t((m0 + arow + 32 * i) * k * 2 + apiece * 16) : kNoLoad;
   const uint32_t a_dst = uint32_t(kAOff + arow * kARowLds + apiece * 16);
-  // code staging: 16-byte piece p = row p / 2, half p % 2 of the tile's
-  // 272 x 32-byte slab of one group; thread tid takes piece tid, and the
-  // first 32 threads also piece 512 + tid (rows 256..271)
+  // code staging, 544 16-byte pieces per group; thread tid takes piece tid,
+  // and the first 32 threads also piece 512 + tid.
+  //   2-bit: piece p = row p / 2, bytes 16 (p % 2) .. of the row's 32.
+  //   base-3: piece p < 272 = bytes 0..15 of row p (-> codes 0..79, code
+  //   bytes 0..19); piece p >= 272 = bytes 10..25 of row p - 272, of which
+  //   bytes 16..25 give codes 80..127 (code bytes 20..31).
   constexpr int kPieces2 = 2 * kTileN - 64 * kWaves;   // 32
   const bool two_pieces = tid < kPieces2;
-  uint32_t c_src[2];
+  uint32_t c_src[2], c_dst[2];
+  bool c_hi[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int pc = tid + 64 * kWaves * i, row = n0 + (pc >> 1);
-    c_src[i] = (i == 0 || two_pieces) && row < n ? uint32_t(row * (k / 4) + 16 * (pc & 1)) : kNoLoad;
+    const int pc = tid + 64 * kWaves * i;
+    const bool hi = PACK == 0 ? (pc & 1) != 0 : pc >= kTileN;
+    const int lrow = PACK == 0 ? pc >> 1 : (hi ? pc - kTileN : pc), row = n0 + lrow;
+    const uint32_t off = PACK == 0 ? 16u * hi : 10u * hi;
+    c_src[i] = (i == 0 || two_pieces) && row < n ? uint32_t(row) * row_bytes + off : kNoLoad;
+    c_dst[i] = uint32_t(kCOff + lrow * kCodeRow + (PACK == 0 ? 16 : 20) * hi);
+    c_hi[i] = hi;
   }
-  const uint32_t c_dst = uint32_t(kCOff + tid * 16);   // piece p sits at 16 p
+  const uint32_t tabc = uint32_t(128 + 4 * (lane & 31));   // base-3 code-field copy of this lane
   // scale staging: element e = tid + 512 i of a 272 x 8 chunk: row e / 8,
   // group 8 chunk + e % 8 (eight threads read a row's 16 contiguous bytes)
   constexpr int kSElems = kTileN * kSChunk;             // 2176
@@ -229,7 +264,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   const uint32_t code_rd16 = uint32_t(kCOff + (256 + nl) * kCodeRow + 8 * q);
   const uint32_t scale_rd = uint32_t(kSOff + (64 * wn + nl) * kSChunk * 2);
   const uint32_t scale_rd16 = uint32_t(kSOff + (256 + nl) * kSChunk * 2);
-  const uint32_t tab = uint32_t(8 * (lane & 31));
+  const uint32_t tab = uint32_t(8 * (lane & (PACK == 0 ? 31 : 15)));
   // A operand read: row nl of each M-block (rotated order), K-slots 32q + 8kc .. of the group
   uint32_t a_addr[4];
 #pragma unroll
@@ -253,11 +288,45 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       rc[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          wrs, c_src[i] == kNoLoad || !live ? kNoLoad : c_src[i] + g * kCodeRow, 0, 0);
+          wrs, c_src[i] == kNoLoad || !live ? kNoLoad : c_src[i] + g * group_bytes, 0, 0);
+  };
+  // base-3 piece -> code dwords: the 10-bit code field of byte j lands at bit
+  // 10 (j - J0) of the piece's code run
+  auto b3_field = [&](const u32x4& v, int j) -> uint32_t {
+    const uint32_t w = v[j >> 2];
+    return lds_read<uint32_t>(__builtin_amdgcn_perm(tabc, w, 0x0C0C0004u | (uint32_t(j & 3) << 8)));
+  };
+  auto store_piece = [&](uint32_t dst, const u32x4& v, bool hi) {
+    if constexpr (PACK == 0) {
+      lds_write<u32x4>(dst, v);
+    } else if (!hi) {
+      uint32_t o[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t f = b3_field(v, j);
+        const int bit = 10 * j;
+        o[bit >> 5] |= f << (bit & 31);
+        if ((bit & 31) > 22) o[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+      }
+      lds_write<u32x4>(dst, u32x4{o[0], o[1], o[2], o[3]});
+      lds_write<uint32_t>(dst + 16, o[4]);
+    } else {
+      uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 6; j < 16; ++j) {
+        const uint32_t f = b3_field(v, j);
+        const int bit = 10 * (j - 6);
+        o[bit >> 5] |= f << (bit & 31);
+        if ((bit & 31) > 22) o[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+      }
+      // bits 96..99 are the group's two pad trits
+      lds_write<uint32_t>(dst, o[0]);
+      lds_write<u32x2>(dst + 4, u32x2{o[1], o[2]});
+    }
   };
   auto store_codes = [&](int buf, const u32x4 (&rc)[2]) {
-    lds_write<u32x4>(c_dst + buf * kCBuf, rc[0]);
-    if (two_pieces) lds_write<u32x4>(c_dst + buf * kCBuf + 64 * kWaves * 16, rc[1]);
+    store_piece(c_dst[0] + buf * kCBuf, rc[0], c_hi[0]);
+    if (two_pieces) store_piece(c_dst[1] + buf * kCBuf, rc[1], c_hi[1]);
   };
   auto load_scales = [&](int chunk, uint32_t (&rs)[5]) {
     const bool live = kSChunk * chunk + sj < groups;
@@ -297,15 +366,21 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   load_a(0, ra);
   load_codes(0, rc);
   {
-    // table: thread -> entry tid / 2, half of its 32 copies
+    // table: thread -> entry tid / 2, one 128-byte half of it (2-bit: 16 of
+    // the 32 fp16 copies; base-3: the 16 fp16 copies, or the 32 code fields)
     const u32x2 v = trit_halves(uint32_t(tid >> 1));
     const uint32_t v0 = v[0], v1 = v[1];
-    const u32x4 v2 = u32x4{v0, v1, v0, v1};
+    u32x4 v2 = u32x4{v0, v1, v0, v1};
+    if (PACK == 1 && (tid & 1)) {
+      const uint32_t f = base3_codes(uint32_t(tid >> 1));
+      v2 = u32x4{f, f, f, f};
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) lds_write<u32x4>(uint32_t(256 * (tid >> 1) + 128 * (tid & 1) + 16 * i), v2);
   }
   store_scales(0, rs);
   store_a(0, ra);
+  if constexpr (PACK == 1) __syncthreads();   // the code-field table is read by the conversion
   store_codes(0, rc);
   load_a(1, ra);
   load_codes(1, rc);
@@ -373,18 +448,25 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
 
 }  // namespace
 
-void launch_gemm(const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y, int m,
-                 int n, int k, hipStream_t s) {
+template <int PACK>
+void launch_pack(const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y, int m, int n, int k,
+                 hipStream_t s) {
   static bool attr = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<PACK>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     return true;
   }();
   (void)attr;
   const int tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
   const int tiles = tiles_m * tiles_n;
-  gemm_t2_kernel<<<dim3(unsigned(tiles)), dim3(64 * kWaves), kLds, s>>>(packed, scales, xr, y, m, n, k, tiles_m,
-                                                                       tiles);
+  gemm_t2_kernel<PACK><<<dim3(unsigned(tiles)), dim3(64 * kWaves), kLds, s>>>(packed, scales, xr, y, m, n, k,
+                                                                             tiles_m, tiles);
+}
+
+void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y, int m,
+                 int n, int k, hipStream_t s) {
+  if (packing == 0) launch_pack<0>(packed, scales, xr, y, m, n, k, s);
+  else launch_pack<1>(packed, scales, xr, y, m, n, k, s);
 }
 
 }  // namespace tb

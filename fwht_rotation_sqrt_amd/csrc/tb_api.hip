@@ -114,13 +114,13 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
 
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream) {
-  if (packing != TB_PACK_2BIT) return TB_ERR_UNSUPPORTED;
+  if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K <= 0 || K % tb::kGroup != 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return TB_ERR_SHAPE;
   if (M == 0 || N == 0) return TB_OK;
   if (!packed || !scales || !xr_f16 || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr_f16) || !aligned16(y)) return TB_ERR_ALIGN;
-  tb::launch_gemm(packed, scales, xr_f16, y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
+  tb::launch_gemm(packing, packed, scales, xr_f16, y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
   return finish_launch();
 }
 

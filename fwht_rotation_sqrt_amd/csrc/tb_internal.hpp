@@ -22,7 +22,7 @@ void launch_fwht(const void* x, int x_dt, void* y, int y_dt, int64_t rows, int64
                  const uint32_t* sign_bits, hipStream_t s);
 void launch_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
                  int xr_dt, float* y, int b, int n, int k, hipStream_t s);
-void launch_gemm(const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y,
+void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y,
                  int m, int n, int k, hipStream_t s);
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);

@@ -130,9 +130,11 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
 /* Prefill product Y = X' W_hat^T for many rows: Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k].
  * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
  * reach 1.76 bit" and "Throughput" (pp512 prompt processing).
- * packing: TB_PACK_2BIT (TB_PACK_BASE3 returns TB_ERR_UNSUPPORTED for now).
+ * packing: TB_PACK_2BIT or TB_PACK_BASE3; packed [N][tb_packed_row_bytes(packing, K)]
+ * as written by tb_pack_2bit / tb_pack_base3 (any address alignment for base-3
+ * rows is handled; the buffer itself 16-byte aligned); scales [N][K/128].
  * xr_f16: fp16 [M][K]; y: fp32 [M][N], overwritten.  Products t*s are exact in
- * fp16; accumulation is fp32 on the matrix cores. */
+ * fp16; accumulation is fp32 on the matrix cores.  K % 128 == 0. */
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream);
 

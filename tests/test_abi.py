@@ -118,7 +118,8 @@ def test_linear_validation():
 def test_gemm_validation():
     lib = tb.library()
     g = lib.tb_gemm
-    assert g(1, P, P, P, P, 4, 8, 128, None) == UNSUP
+    assert g(2, P, P, P, P, 4, 8, 128, None) == UNSUP
+    assert g(1, P, P, P, P, 4, 8, 100, None) == SHAPE
     assert g(0, P, P, P, P, 4, 8, 100, None) == SHAPE
     assert g(0, P, P, P, P, -4, 8, 128, None) == SHAPE
     assert g(0, None, P, P, P, 4, 8, 128, None) == NULL

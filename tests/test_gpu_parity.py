@@ -214,31 +214,46 @@ def test_linear_fused_rotation(packing, n, k, x_dtype):
 
 # ------------------------------------------------------------------ prefill product
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 37, 1024), (64, 64, 256), (100, 300, 2048), (130, 1000, 5120)])
-def test_gemm_small_shapes(m, n, k):
-    note(f"gemm m={m} n={n} k={k}")
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 37, 1024), (64, 64, 256), (100, 300, 2048), (130, 1000, 5120),
+                                   (129, 545, 1152), (7, 273, 640)])
+def test_gemm_small_shapes(packing, m, n, k):
+    note(f"gemm {packing} m={m} n={n} k={k}")
     g = synth.rng(230, 0, m % 251, n % 251)
     t = synth.trits(g, n, k)
     s = synth.scales_f16(g, n, k)
     xr = g.standard_normal((m, k)).astype(np.float16)
-    packed, _ = oracle.pack_2bit(t)
-    want = oracle.gemm("2bit", packed, s, xr.astype(np.float64), k)
-    got = host(tb.tb_gemm("2bit", dev(packed), scales_dev(s), dev(xr)))
+    packed, _ = PACK_REF[packing](t)
+    want = oracle.gemm(packing, packed, s, xr.astype(np.float64), k)
+    got = host(tb.tb_gemm(packing, dev(packed), scales_dev(s), dev(xr)))
     assert oracle.rel_err(got, want) < TOL
 
 
-def test_gemm_pp512_end_to_end():
-    note("pp512 GEMM M=512 N=17408 K=5120 2-bit, bf16 activations with outliers")
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_gemm_pp512_end_to_end(packing):
+    note(f"pp512 GEMM M=512 N=17408 K=5120 {packing}, bf16 activations with outliers")
     m, n, k = 512, synth.FFN, synth.HIDDEN
     li = _linear(3, n, k, m, "bf16", True)
-    ref_packed, _ = oracle.pack_2bit(li.trits)
-    packed = tb.tb_pack_2bit(dev(li.trits))
+    ref_packed, _ = PACK_REF[packing](li.trits)
+    packed = (tb.tb_pack_2bit if packing == "2bit" else tb.tb_pack_base3)(dev(li.trits))
     assert np.array_equal(host(packed), ref_packed)
     xr_exact = oracle.rotate(act_f64(li.x, "bf16"), li.signs)
-    want = oracle.gemm("2bit", ref_packed, li.scales, xr_exact.astype(np.float16).astype(np.float64), k)
+    want = oracle.gemm(packing, ref_packed, li.scales, xr_exact.astype(np.float16).astype(np.float64), k)
     xr = tb.tb_fwht_rotate(act_dev(li.x, "bf16"), signs_dev(li.signs), torch.float16)
-    y = host(tb.tb_gemm("2bit", packed, scales_dev(li.scales), xr))
+    y = host(tb.tb_gemm(packing, packed, scales_dev(li.scales), xr))
     assert oracle.rel_err(y, want) < TOL
     # against the unrounded product too: fp16 rounding of X' stays inside the bound
-    want_exact = oracle.gemm("2bit", ref_packed, li.scales, xr_exact, k)
+    want_exact = oracle.gemm(packing, ref_packed, li.scales, xr_exact, k)
     assert oracle.rel_err(y, want_exact) < TOL
+
+
+def test_gemm_base3_equals_2bit():
+    note("gemm base-3 and 2-bit of the same trits agree exactly")
+    g = synth.rng(231, 0, 0, 0)
+    m, n, k = 96, 300, 1280
+    t = synth.trits(g, n, k)
+    s = scales_dev(synth.scales_f16(g, n, k))
+    xr = dev(g.standard_normal((m, k)).astype(np.float16))
+    y2 = host(tb.tb_gemm("2bit", dev(oracle.pack_2bit(t)[0]), s, xr))
+    y3 = host(tb.tb_gemm("base3", dev(oracle.pack_base3(t)[0]), s, xr))
+    assert np.array_equal(y2, y3)
