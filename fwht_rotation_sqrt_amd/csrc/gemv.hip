@@ -11,7 +11,10 @@
 //     - sum_k x_k (the activation sum is kept per group).
 //   * base-3 bytes: one LDS table lookup turns a byte into a dword holding the
 //     nibbles of its five trits themselves (-1.0, 0, +1.0); the table has 32
-//     bank-spread copies so a wave's lookups do not conflict.
+//     bank-spread copies so a wave's lookups do not conflict.  The 128 trits
+//     of a group fill the 128 K-slots of one matrix instruction densely (the
+//     group's two pad trits are left out), so a group costs one instruction,
+//     as for 2-bit codes.
 // The activations become three fp8 (e4m3) limbs per element, per 128-group
 // scaled by a power of two so the largest magnitude lies in [128, 256):
 //   x * 2^sig = l0 + l1/16 + l2/256, each limb the e4m3 rounding of what is
@@ -54,7 +57,7 @@ constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past any buffer: rea
 template <int PACK>
 struct Fmt {
   static constexpr int kGroupBytes = PACK == 0 ? 32 : kB3GroupBytes;
-  static constexpr int kMfmas = PACK == 0 ? 1 : 2;             // matrix instructions per group
+  static constexpr int kMfmas = 1;                             // matrix instructions per group
   static constexpr int kRowStage = kGroupBytes * kStageGroups;  // 256 or 208 bytes of a row per stage
   // LDS row stride: 66 or 54 dwords, so the 16 rows a quarter-wave reads
   // (two dwords each) fall in distinct banks
@@ -97,13 +100,20 @@ __device__ __forceinline__ int slot_of(int tau, int* mi) {
     *mi = 0;
     return 32 * q + 8 * w + ((r & 15) >> 1);
   } else {
-    // byte p = tau / 5 goes to instruction p / 16, lane group (p % 16) / 4,
-    // dword p % 4; digit d = tau % 5 is nibble d of that dword.
-    const int p = tau / 5, d = tau - 5 * p;
-    *mi = p >> 4;
-    const int pp = p & 15;
-    return 32 * (pp >> 2) + 8 * (pp & 3) + d;
+    // lane group q takes trits 30q .. 30q + 29 (bytes 6q .. 6q + 5) in its
+    // slots 0..29 and trits 120 + 2q, 121 + 2q (from bytes 24 and 25) in
+    // slots 30, 31
+    *mi = 0;
+    if (tau < 120) return 32 * (tau / 30) + tau % 30;
+    const int u = tau - 120;
+    return 32 * (u >> 1) + 30 + (u & 1);
   }
+}
+
+// Trit (0..127) of a group that sits in K-slot s: the inverse of slot_of for
+// the base-3 layout.
+__host__ __device__ constexpr int b3_tau_of_slot(int s) {
+  return (s & 31) < 30 ? 30 * (s >> 5) + (s & 31) : 120 + 2 * (s >> 5) + ((s & 31) - 30);
 }
 
 // LDS of a workgroup, in this order: the base-3 table (at address 0, so a
@@ -152,29 +162,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
 }
 
-// Elements of a (batch, group) that thread l16 of its team of 16 converts:
+// Elements of a (batch, group) that thread l16 of its team of 16 converts, as
+// four pairs of consecutive elements:
 //   2-bit: 8 consecutive elements 8 l16 ..; they land in two limb dwords.
-//   base-3: the 10 digits of code bytes 2 l16 and 2 l16 + 1 (elements 10 l16
-//   ..; those past 127 are the pad digits, taken as 0), one 16-byte block of
-//   each limb row.  Threads 13..15 cover bytes 26..31 with zeros, so every
-//   K-slot the matrix instructions read is written.
+//   base-3: the trits of K-slots 8 l16 .. 8 l16 + 7, which land in one limb
+//   qword; pair e starts at trit b3_tau_of_slot(8 l16 + 2 e).
 template <int PACK>
 struct XMap {
-  static constexpr int kElems = PACK == 0 ? 8 : 10;
-  static __device__ __forceinline__ int first(int l16) { return PACK == 0 ? 8 * l16 : 10 * l16; }
+  static constexpr int kElems = 8;
+  static __device__ __forceinline__ int pair(int l16, int e) {
+    return PACK == 0 ? 8 * l16 + 2 * e : b3_tau_of_slot(8 * l16 + 2 * e);
+  }
 };
 
 template <int XDT, int PACK>
 __device__ __forceinline__ void load_x(const void* __restrict__ xr, int k, int b, int g, int l16, float (&x)[10]) {
   const int64_t row = int64_t(b) * k + int64_t(g) * kGroup;
-  const int first = XMap<PACK>::first(l16);
+  x[8] = x[9] = 0.f;
 #pragma unroll
-  for (int e = 0; e < 5; ++e) {
-    if (2 * e >= XMap<PACK>::kElems) {
-      x[2 * e] = x[2 * e + 1] = 0.f;
-      continue;
-    }
-    const int idx = first + 2 * e;
+  for (int e = 0; e < 4; ++e) {
+    const int idx = XMap<PACK>::pair(l16, e);
     const int ic = min(idx, kGroup - 2);  // in-bounds address; the value is dropped below
     float2 v;
     if constexpr (XDT == 0) {
@@ -280,14 +287,14 @@ __device__ __forceinline__ void rotate_block(float (&v)[16], float* L, int lane)
 // same assignment as load_x.
 template <int PACK>
 __device__ __forceinline__ void load_x_rot(const float* L, int gi, int l16, float (&x)[10]) {
-  const int first = XMap<PACK>::first(l16);
 #pragma unroll
-  for (int e = 0; e < 10; ++e) {
-    const int t = first + e;
+  for (int e = 0; e < 8; ++e) {
+    const int t = XMap<PACK>::pair(l16, e >> 1) + (e & 1);
     const int i = gi * kGroup + min(t, kGroup - 1);
     const float v = L[i + (i >> 4)];
-    x[e] = (e < XMap<PACK>::kElems && t < kGroup) ? v : 0.f;
+    x[e] = t < kGroup ? v : 0.f;
   }
+  x[8] = x[9] = 0.f;
 }
 
 // Butterfly reductions over the 16 lanes of a DPP row (a team), no LDS.
@@ -345,9 +352,8 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
     rowbase = sm.a + b * sm.a_bstride + g * kAGroup;
     off = 32 * (l16 >> 2) + 16 * ((l16 & 3) >> 1) + 4 * (l16 & 1);
   } else {
-    const int p0 = 2 * l16, mi = p0 >> 4, pp = p0 & 15;
-    rowbase = sm.a + b * sm.a_bstride + (g * 2 + mi) * kAGroup;
-    off = 32 * (pp >> 2) + 8 * (pp & 3);
+    rowbase = sm.a + b * sm.a_bstride + g * kAGroup;
+    off = 8 * l16;
   }
   constexpr float kW[3] = {1.f, 0.0625f, 0.00390625f};
 #pragma unroll
@@ -366,19 +372,15 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
       *reinterpret_cast<uint32_t*>(dst) = uint32_t(de);
       *reinterpret_cast<uint32_t*>(dst + 8) = uint32_t(dd);
     } else {
-      // byte 2 l16: digits in slots off..off+4, byte 2 l16 + 1: off+8..off+12;
-      // slots 5..7 of each 8-slot block hold zero
+      // the thread's 8 K-slots in order: one qword
       int d0 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[0], cur[1], 0, false);
       d0 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[2], cur[3], d0, true);
-      const int d1 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[4], 0.f, 0, false);
-      int d2 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[5], cur[6], 0, false);
-      d2 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[7], cur[8], d2, true);
-      const int d3 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[9], 0.f, 0, false);
+      int d1 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[4], cur[5], 0, false);
+      d1 = __builtin_amdgcn_cvt_pk_fp8_f32(cur[6], cur[7], d1, true);
       fp8x4_to_f32<0, 1>(d0, a);
-      fp8x4_to_f32<5, 1>(d2, a);
-      a[4] = __builtin_amdgcn_cvt_f32_fp8(d1, 0);
-      a[9] = __builtin_amdgcn_cvt_f32_fp8(d3, 0);
-      *reinterpret_cast<uint4*>(dst) = make_uint4(uint32_t(d0), uint32_t(d1), uint32_t(d2), uint32_t(d3));
+      fp8x4_to_f32<4, 1>(d1, a);
+      a[8] = a[9] = 0.f;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(uint32_t(d0), uint32_t(d1));
     }
 #pragma unroll
     for (int e = 0; e < 10; ++e) {
@@ -397,7 +399,11 @@ struct LaneCtx {
   int b_row;      // byte offset of this lane's staged row and K-part (B operand)
   int a_lane[2];  // per row set: LDS address of this lane's A-operand row in group 0
   int f_lane[2];  // per row set: index of this lane's batch row in f
-  uint32_t tab;   // base-3 table: this lane's copy offset 4 * (lane & 15) in byte 0
+  uint32_t tab;   // base-3 table: this lane's copy offset 4 * (lane & 31) in byte 0
+  // base-3, by group parity P: dword-aligned offset of bytes 6q .. 6q + 5 of
+  // the group from the pair's start, and their byte shift in that dword
+  uint32_t b3_off[2], b3_sh[2];
+  uint32_t q8;    // 8 * lane group: which two of the ten extra trits are this lane's
 };
 
 // Raw staged bytes of group g for this lane, from bo = b_row + group-bytes *
@@ -406,27 +412,29 @@ struct LaneCtx {
 //   base-3: the aligned dword pairs around its 4-byte pieces of the two
 //   instructions (odd groups start 2 bytes into a dword; realigned in make_bop).
 template <int PACK, int P>
-__device__ __forceinline__ void read_group_bytes(uint32_t bo, uint32_t (&raw)[4]) {
+__device__ __forceinline__ void read_group_bytes(const LaneCtx& lc, uint32_t bo, uint32_t (&raw)[4]) {
   if constexpr (PACK == 0) {
     const u32x2 w = lds_read<u32x2, 32 * P>(bo);
     raw[0] = w.x; raw[1] = w.y; raw[2] = 0; raw[3] = 0;
   } else {
-    // rows are only 4-byte aligned here: dword-pair reads
-    constexpr int o = P ? kB3GroupBytes - 2 : 0;
-    raw[0] = lds_read<uint32_t, o>(bo);
-    raw[1] = lds_read<uint32_t, o + 4>(bo);
-    raw[2] = lds_read<uint32_t, o + 16>(bo);
-    raw[3] = lds_read<uint32_t, o + 20>(bo);
+    // the dword pair holding bytes 6q .. 6q + 5 (a group starts 2-byte
+    // aligned), and the dword holding bytes 24 and 25
+    const uint32_t a = bo + lc.b3_off[P];
+    raw[0] = lds_read<uint32_t>(a);
+    raw[1] = lds_read<uint32_t, 4>(a);
+    raw[2] = lds_read<uint32_t, P ? 48 : 24>(bo);
+    raw[3] = 0;
   }
 }
 
 // B operand(s) from the raw bytes of a group of parity P.
 //   * 2-bit: the 2-bit codes already are e2m1 nibbles for c/2; even and odd
 //     codes of each dword go to separate dwords.
-//   * base-3: one table lookup per byte; the address (byte << 8) | copy is
-//     formed by one byte permute.  Bytes past the group's 26 (and the two pad
-//     digits of byte 25) meet all-zero activation slots, and fp4 has no NaN,
-//     so they add 0.  Nibbles 5..7 of each looked-up dword are zero.
+//   * base-3: one table lookup per byte (its five trits as nibbles 0..4 of a
+//     dword, nibbles 5..7 zero); the address (byte << 8) | copy is formed by
+//     one byte permute.  Lane group q's 32 nibbles are the trits of bytes
+//     6q .. 6q + 5 (slots 0..29) and two of the ten trits of bytes 24, 25
+//     (slots 30, 31; the last two of the ten are the group's pads).
 template <int PACK, int P>
 __device__ __forceinline__ void make_bop(const Smem& sm, const LaneCtx& lc, const uint32_t (&raw)[4],
                                          v8i (&bop)[Fmt<PACK>::kMfmas]) {
@@ -434,19 +442,21 @@ __device__ __forceinline__ void make_bop(const Smem& sm, const LaneCtx& lc, cons
     const uint32_t m = 0x33333333u;
     bop[0] = v8i{int(raw[0] & m), int((raw[0] >> 2) & m), int(raw[1] & m), int((raw[1] >> 2) & m), 0, 0, 0, 0};
   } else {
-    const uint32_t by[2] = {__builtin_amdgcn_alignbyte(raw[1], raw[0], 2 * P),
-                            __builtin_amdgcn_alignbyte(raw[3], raw[2], 2 * P)};
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      int dw[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // address bytes: [0] = lane copy offset, [1] = code byte w, [2..3] = 0
-        const uint32_t addr = __builtin_amdgcn_perm(lc.tab, by[mi], 0x0C0C0004u | (uint32_t(w) << 8));
-        dw[w] = lds_read<int>(addr);
-      }
-      bop[mi] = v8i{dw[0], dw[1], dw[2], dw[3], 0, 0, 0, 0};
-    }
+    // bytes 6q .. 6q + 3 in w0, 6q + 4 and 6q + 5 in the low half of w1
+    const uint32_t sh = lc.b3_sh[P];
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);
+    const uint32_t w1 = raw[1] >> (8 * sh);
+    auto look = [&](uint32_t w, int byte) -> uint32_t {
+      // address bytes: [0] = lane copy offset, [1] = the code byte, [2..3] = 0
+      return lds_read<uint32_t>(__builtin_amdgcn_perm(lc.tab, w, 0x0C0C0004u | (uint32_t(byte) << 8)));
+    };
+    const uint32_t e0 = look(w0, 0), e1 = look(w0, 1), e2 = look(w0, 2), e3 = look(w0, 3);
+    const uint32_t e4 = look(w1, 0), e5 = look(w1, 1);
+    // bytes 24 and 25: byte 0 and 1 (even group) or 2 and 3 (odd group) of raw[2]
+    const uint32_t e24 = look(raw[2], P ? 2 : 0), e25 = look(raw[2], P ? 3 : 1);
+    const uint32_t extra = ((e24 | (e25 << 20)) >> lc.q8) & 0xFFu;
+    bop[0] = v8i{int(e0 | (e1 << 20)), int((e1 >> 12) | (e2 << 8) | (e3 << 28)), int((e3 >> 4) | (e4 << 16)),
+                 int((e4 >> 16) | (e5 << 4) | (extra << 24)), 0, 0, 0, 0};
   }
 }
 
@@ -539,8 +549,8 @@ __device__ __forceinline__ void group_step(const Smem& sm, const LaneCtx& lc, ui
   v8i aops[NR][F::kMfmas];
   load_aop<PACK, NR>(lc, gc, aops);
   // the next group's bytes (past the stage's last group: the row padding, ignored)
-  if constexpr (P == 0) read_group_bytes<PACK, 1>(bo, st.raw[1]);
-  else read_group_bytes<PACK, 0>(bo + 2 * F::kGroupBytes, st.raw[0]);
+  if constexpr (P == 0) read_group_bytes<PACK, 1>(lc, bo, st.raw[1]);
+  else read_group_bytes<PACK, 0>(lc, bo + 2 * F::kGroupBytes, st.raw[0]);
   float ccur[NR];
   group_consts<PACK, NR, P>(sm, lc, sq0, gc, ccur, yacc);
   v4f cur[NR];
@@ -568,7 +578,7 @@ __device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, co
   }
   uint32_t sq[4] = {sreg[0], sreg[1], sreg[2], sreg[3]};
   uint32_t bo = stage + lc.b_row;
-  read_group_bytes<PACK, 0>(bo, st.raw[0]);
+  read_group_bytes<PACK, 0>(lc, bo, st.raw[0]);
   int g = 0;
 #pragma unroll 1
   for (; g + 1 < sg; g += 2) {
@@ -698,7 +708,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   uint8_t* my_stage = sm.stage + wave * F::kStageLds;
   const uint32_t my_stage_addr = uint32_t(F::kTable + a_bytes + f_region_bytes(nb, ng) + wave * F::kStageLds);
   LaneCtx lc;
-  lc.b_row = nl * F::kRowLds + (PACK == 0 ? 8 * q : 4 * q);
+  lc.b_row = nl * F::kRowLds + (PACK == 0 ? 8 * q : 0);
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int o = kB3GroupBytes * par + 6 * q;   // even: 0, 6, 12, 18; odd: 26, 32, 38, 44
+    lc.b3_off[par] = uint32_t(o & ~3);
+    lc.b3_sh[par] = uint32_t(o & 3);
+  }
+  lc.q8 = uint32_t(8 * q);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     // A rows are 4b + limb; unused rows (limb 3, or batch >= nb) read a valid
