@@ -726,9 +726,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   }
   lc.tab = uint32_t(4 * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
 
-  // ---- roles.  The first prep_waves waves build the activation limbs (and
-  // the base-3 table) and only then load weights; the others start the weight
-  // stream at once.  A wave starts its matrix work when the LDS counter shows
+  // ---- roles.  The first prep_waves waves build the activation limbs and
+  // only then load weights; the others (after the base-3 table, when they
+  // write it) start the weight stream at once.  A wave starts its matrix work when the LDS counter shows
   // every prep wave done, not at a workgroup barrier, so it never waits for
   // another wave's weight loads to be issued.
   const int pairs = ng * nb;
@@ -739,13 +739,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
                              : min(nwaves, (pairs + 11) / 12);  // ~3 (batch, group) pairs per team
   const bool prep = wave < prep_waves;
   const int team = tid / kTeam, l16 = tid % kTeam, nteams = prep_waves * (64 / kTeam);
+  // The base-3 decode table is written by the waves that build no limbs
+  // (they would otherwise sit idle until the limbs are ready), or by the prep
+  // waves when every wave is one.  Each table wave adds 1 to the ready count.
+  const bool tab_by_rest = PACK == 1 && nwaves > prep_waves;
+  const int ready_target = prep_waves + (tab_by_rest ? nwaves - prep_waves : 0);
   float xa[10], xb[10], xc[10];
   float va[16];
+  uint32_t sw_next = 0;  // sign words of the rotation unit about to be rotated
   if constexpr (ROT) {
     if (prep) {
-      // the first unit's activations go out before any weight load
+      // the first unit's activations and sign words go out before any weight load
       const int b = wave % nb, blk = wave / nb;
       load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
+      sw_next = sign_bits[((g_begin >> 3) + blk) * 32 + (lane >> 1)];
     }
   } else if (prep) {
     // the activation loads go out before any weight load of the workgroup
@@ -780,7 +787,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   uint4 stg[kDepth][F::kLoads];
   uint32_t scl[kDepth][4];
   if (prep) {
-    if constexpr (PACK == 1) {
+    if (PACK == 1 && !tab_by_rest) {
       for (int e = tid; e < 256; e += 64 * prep_waves) {
         const uint32_t v = base3_t_nibbles(uint32_t(e));
         uint4* dst = reinterpret_cast<uint4*>(sm.lds + 256 * e);
@@ -796,10 +803,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
       const int tw = lane >> 4;
       for (int u = wave; u < units; u += prep_waves) {
         const int b = u % nb, blk = u / nb;
-        if (u != wave)
+        if (u != wave) {
           load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
-        const int beta = (g_begin >> 3) + blk;  // block index in the row
-        const uint32_t sw = sign_bits[beta * 32 + (lane >> 1)] >> ((lane & 1) * 16);
+          sw_next = sign_bits[((g_begin >> 3) + blk) * 32 + (lane >> 1)];  // this block's sign words
+        }
+        const uint32_t sw = sw_next >> ((lane & 1) * 16);
 #pragma unroll
         for (int j = 0; j < 16; ++j) va[j] = __uint_as_float(__float_as_uint(va[j]) ^ (((sw >> j) & 1u) << 31));
         rotate_block(va, L, lane);
@@ -826,12 +834,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+  if (PACK == 1 && tab_by_rest && !prep) {
+    // the table comes before this wave's weight loads: the loads would delay
+    // it (it gates every wave's matrix work) more than it delays them
+    for (int e = tid - 64 * prep_waves; e < 256; e += 64 * (nwaves - prep_waves)) {
+      const uint32_t v = base3_t_nibbles(uint32_t(e));
+      uint4* dst = reinterpret_cast<uint4*>(sm.lds + 256 * e);
+#pragma unroll
+      for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the table writes come before the count
+    if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
     issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s_lo + d, s_full, stg[d], scl[d]);
-  // every prep wave has finished (each adds 1 exactly once, and none waits
-  // on anything, so this ends)
-  while (__hip_atomic_load(sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < prep_waves)
+  // every prep wave (and table wave) has finished (each adds 1 exactly once,
+  // and none waits on anything, so this ends)
+  while (__hip_atomic_load(sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < ready_target)
     __builtin_amdgcn_s_sleep(1);
 
 
