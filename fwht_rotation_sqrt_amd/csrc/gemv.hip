@@ -26,9 +26,10 @@
 //
 // Work split: a workgroup of up to 16 waves holds rt tiles of 16 weight rows;
 // the 8-group stages (1024 weights per row) of a tile are split over ks waves.
-// A wave's packed bytes stream through registers kDepth stages ahead with
-// coalesced 16-byte buffer loads, go to a per-wave LDS buffer and are read
-// back in the operand layout.  A few "prep" waves turn the activations into
+// A wave's packed bytes stream through registers with coalesced 16-byte
+// buffer loads (a stage's loads go out before the matrix work of the stage
+// before it), go to a per-wave LDS buffer and are read back in the operand
+// layout.  A few "prep" waves turn the activations into
 // limbs in LDS (for as many groups as fit; larger K takes several launches)
 // while the other waves already stream weights.
 #include "tb_internal.hpp"
@@ -44,7 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;       // waves per workgroup
-constexpr int kDepth = 2;           // staged stages in flight per wave (registers)
+
 constexpr int kStageGroups = 8;     // groups per stage (1024 weights per row)
 constexpr int kCopies = 32;         // bank-spread copies of the base-3 table (one per half-wave lane)
 constexpr int kLdsBytes = 160 * 1024;
@@ -58,6 +59,10 @@ template <int PACK>
 struct Fmt {
   static constexpr int kGroupBytes = PACK == 0 ? 32 : kB3GroupBytes;
   static constexpr int kMfmas = 1;                             // matrix instructions per group
+  // register slots of staged stages per wave: 2-bit stages load while the
+  // stage before them computes (one slot); base-3 stages two ahead (two
+  // slots, refilled after the compute)
+  static constexpr int kDepth = PACK == 0 ? 1 : 2;
   static constexpr int kRowStage = kGroupBytes * kStageGroups;  // 256 or 208 bytes of a row per stage
   // LDS row stride: 66 or 54 dwords, so the 16 rows a quarter-wave reads
   // (two dwords each) fall in distinct banks
@@ -66,7 +71,7 @@ struct Fmt {
   static constexpr int kStageChunks = 16 * kChunksPerRow;       // 256 or 208
   static constexpr int kLoads = (kStageChunks + 63) / 64;       // 4
   static constexpr int kStageLds = 16 * kRowLds + 32;           // + pad for operand over-reads
-  // base-3 table: entry e at byte 256 e, copy c (lane & 15) at + 4c, so one
+  // base-3 table: entry e at byte 256 e, copy c (lane & 31) at + 4c, so one
   // byte permute forms the address (e << 8) | 4c from the staged bytes
   static constexpr int kTable = PACK == 1 ? 256 * 256 : 0;
 };
@@ -155,6 +160,15 @@ __device__ __forceinline__ uint32_t base3_t_nibbles(uint32_t e) {
     e /= 3u;
   }
   return v;
+}
+
+// Table entry e at LDS byte 256 e: kCopies copies of its trit nibbles, one
+// per lane of a half-wave, so the lanes' lookups fall in distinct banks.
+__device__ __forceinline__ void write_b3_entry(uint8_t* lds, uint32_t e) {
+  const uint32_t v = base3_t_nibbles(e);
+  uint4* dst = reinterpret_cast<uint4*>(lds + 256 * e);
+#pragma unroll
+  for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -396,181 +410,238 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
 
 // Per-lane constants of the matrix work.
 struct LaneCtx {
-  int b_row;      // byte offset of this lane's staged row and K-part (B operand)
+  int b_row;      // byte offset of this lane's staged row (2-bit: plus its 8q code bytes)
   int a_lane[2];  // per row set: LDS address of this lane's A-operand row in group 0
   int f_lane[2];  // per row set: index of this lane's batch row in f
   uint32_t tab;   // base-3 table: this lane's copy offset 4 * (lane & 31) in byte 0
-  // base-3, by group parity P: dword-aligned offset of bytes 6q .. 6q + 5 of
-  // the group from the pair's start, and their byte shift in that dword
+  // base-3, by group parity P: offset of the dword pair holding bytes
+  // 6q .. 6q + 5 from the group pair's start, and their shift in bytes
+  // within it (0 or 2)
   uint32_t b3_off[2], b3_sh[2];
   uint32_t q8;    // 8 * lane group: which two of the ten extra trits are this lane's
 };
 
-// Raw staged bytes of group g for this lane, from bo = b_row + group-bytes *
-// (the even group of the pair) and the group's parity P.
-//   2-bit: the two dwords of its 32 codes;
-//   base-3: the aligned dword pairs around its 4-byte pieces of the two
-//   instructions (odd groups start 2 bytes into a dword; realigned in make_bop).
-template <int PACK, int P>
-__device__ __forceinline__ void read_group_bytes(const LaneCtx& lc, uint32_t bo, uint32_t (&raw)[4]) {
-  if constexpr (PACK == 0) {
-    const u32x2 w = lds_read<u32x2, 32 * P>(bo);
-    raw[0] = w.x; raw[1] = w.y; raw[2] = 0; raw[3] = 0;
-  } else {
-    // the dword pair holding bytes 6q .. 6q + 5 (a group starts 2-byte
-    // aligned), and the dword holding bytes 24 and 25
-    const uint32_t a = bo + lc.b3_off[P];
-    raw[0] = lds_read<uint32_t>(a);
-    raw[1] = lds_read<uint32_t, 4>(a);
-    raw[2] = lds_read<uint32_t, P ? 48 : 24>(bo);
-    raw[3] = 0;
-  }
+// A float2 from LDS (vector types have no address-space-qualified copy).
+template <int OFF>
+__device__ __forceinline__ float2 lds_f2(uint32_t addr) {
+  const u32x2 w = lds_read<u32x2, OFF>(addr);
+  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
 }
 
-// B operand(s) from the raw bytes of a group of parity P.
-//   * 2-bit: the 2-bit codes already are e2m1 nibbles for c/2; even and odd
-//     codes of each dword go to separate dwords.
-//   * base-3: one table lookup per byte (its five trits as nibbles 0..4 of a
-//     dword, nibbles 5..7 zero); the address (byte << 8) | copy is formed by
-//     one byte permute.  Lane group q's 32 nibbles are the trits of bytes
-//     6q .. 6q + 5 (slots 0..29) and two of the ten trits of bytes 24, 25
-//     (slots 30, 31; the last two of the ten are the group's pads).
-template <int PACK, int P>
-__device__ __forceinline__ void make_bop(const Smem& sm, const LaneCtx& lc, const uint32_t (&raw)[4],
-                                         v8i (&bop)[Fmt<PACK>::kMfmas]) {
-  if constexpr (PACK == 0) {
-    const uint32_t m = 0x33333333u;
-    bop[0] = v8i{int(raw[0] & m), int((raw[0] >> 2) & m), int(raw[1] & m), int((raw[1] >> 2) & m), 0, 0, 0, 0};
-  } else {
-    // bytes 6q .. 6q + 3 in w0, 6q + 4 and 6q + 5 in the low half of w1
-    const uint32_t sh = lc.b3_sh[P];
-    const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);
-    const uint32_t w1 = raw[1] >> (8 * sh);
-    auto look = [&](uint32_t w, int byte) -> uint32_t {
-      // address bytes: [0] = lane copy offset, [1] = the code byte, [2..3] = 0
-      return lds_read<uint32_t>(__builtin_amdgcn_perm(lc.tab, w, 0x0C0C0004u | (uint32_t(byte) << 8)));
-    };
-    const uint32_t e0 = look(w0, 0), e1 = look(w0, 1), e2 = look(w0, 2), e3 = look(w0, 3);
-    const uint32_t e4 = look(w1, 0), e5 = look(w1, 1);
-    // bytes 24 and 25: byte 0 and 1 (even group) or 2 and 3 (odd group) of raw[2]
-    const uint32_t e24 = look(raw[2], P ? 2 : 0), e25 = look(raw[2], P ? 3 : 1);
-    const uint32_t extra = ((e24 | (e25 << 20)) >> lc.q8) & 0xFFu;
-    bop[0] = v8i{int(e0 | (e1 << 20)), int((e1 >> 12) | (e2 << 8) | (e3 << 28)), int((e3 >> 4) | (e4 << 16)),
-                 int((e4 >> 16) | (e5 << 4) | (extra << 24)), 0, 0, 0, 0};
-  }
-}
+// ---- 2-bit, unrolled group sequence: every offset is an immediate.
 
-// A operands of group gc (lane rows of unused (batch, limb) pairs read a
-// valid limb row: row i of A only feeds row i of the result, never stored).
-template <int PACK, int NR>
-__device__ __forceinline__ void load_aop(const LaneCtx& lc, int gc, v8i (&aops)[NR][Fmt<PACK>::kMfmas]) {
-  using F = Fmt<PACK>;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint32_t ag = uint32_t(lc.a_lane[r] + gc * F::kMfmas * kAGroup);
-    const u32x4 lo0 = lds_read<u32x4, 0>(ag), hi0 = lds_read<u32x4, 64>(ag);
-    aops[r][0] = v8i{int(lo0.x), int(lo0.y), int(lo0.z), int(lo0.w), int(hi0.x), int(hi0.y), int(hi0.z), int(hi0.w)};
-    if constexpr (F::kMfmas == 2) {
-      const u32x4 lo1 = lds_read<u32x4, kAGroup>(ag), hi1 = lds_read<u32x4, kAGroup + 64>(ag);
-      aops[r][1] = v8i{int(lo1.x), int(lo1.y), int(lo1.z), int(lo1.w), int(hi1.x), int(hi1.y), int(hi1.z), int(hi1.w)};
-    }
-  }
-}
-
-template <int PACK, int NR>
-__device__ __forceinline__ void group_mma(const v8i (&aops)[NR][Fmt<PACK>::kMfmas],
-                                          const v8i (&bop)[Fmt<PACK>::kMfmas], v4f (&out)[NR]) {
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    v4f a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mi = 0; mi < Fmt<PACK>::kMfmas; ++mi)
-      a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aops[r][mi], bop[mi], a4, 0, 4, 0, 127, 0, 127);
-    out[r] = a4;
-  }
-}
-
-// Epilogue constants of group gc for this lane's batches: c = s 2^-sig, and
-// for 2-bit codes c = 2 s 2^-sig (the factor 2 turns the nibble values c/2
-// back into codes) with the activation-sum correction -s 2^-sig S added to
-// yacc at once.  The group's
-// fp16 scale is half P of sq0 (the stage's scales of the lane's row, two per
-// dword, advanced one dword per group pair: indexing a register array with
-// the loop counter would put it in scratch memory).
-template <int PACK, int NR, int P>
-__device__ __forceinline__ void group_consts(const Smem& sm, const LaneCtx& lc, uint32_t sq0, int gc,
-                                             float (&c)[NR], float (&yacc)[NR]) {
-  const float sc = float(__builtin_bit_cast(_Float16, uint16_t(P ? sq0 >> 16 : sq0 & 0xFFFFu)));
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float2 fs = sm.f[lc.f_lane[r] + gc];
-    const float cg = sc * fs.x;
-    if constexpr (PACK == 0) {
-      c[r] = 2.f * cg;
-      yacc[r] = fmaf(-cg, fs.y, yacc[r]);
-    } else {
-      c[r] = cg;  // base-3 operands are the trits themselves
-    }
-  }
-}
-
-// y += c * (d0 + d1/16 + d2/256) with d the limb rows of this lane's result
-// (batch 4r + q).  Lanes of batches >= nb accumulate values that are never
-// stored.  No branch here on purpose: a matrix instruction must run with the
-// whole wave active, so its result may not feed a lane-divergent block.
-template <int NR>
-__device__ __forceinline__ void group_epilogue(const v4f (&acc)[NR], const float (&c)[NR], float (&yacc)[NR]) {
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float p = fmaf(acc[r][2], 0.00390625f, fmaf(acc[r][1], 0.0625f, acc[r][0]));
-    yacc[r] = fmaf(c[r], p, yacc[r]);
-  }
-}
-
-// Pipeline state of one stage's group loop.
-template <int PACK, int NR>
-struct GroupPipe {
-  uint32_t raw[2][4];                  // staged bytes of the next groups, by parity
-  v4f prev[NR];                        // matrix results of the previous group
-  float cprev[NR];                     // its epilogue factors
+// Per-stage base addresses: the lane's staged codes, its A row of the
+// stage's first group, and its factor entry of that group.
+struct StageBase {
+  uint32_t row, a[2], f[2];
 };
 
-// One group of parity P: B operands from bytes read one group earlier, the A
-// operands and epilogue constants, the next group's bytes, the matrix
-// instructions, then the previous group's epilogue.  So every dependent LDS
-// round trip except the table lookup is a group ahead of its use.
-template <int PACK, int NR, int P>
-__device__ __forceinline__ void group_step(const Smem& sm, const LaneCtx& lc, uint32_t bo, int gc,
-                                           uint32_t sq0, GroupPipe<PACK, NR>& st, float (&yacc)[NR]) {
-  using F = Fmt<PACK>;
-  __builtin_amdgcn_sched_barrier(0);
-  v8i bop[F::kMfmas];
-  make_bop<PACK, P>(sm, lc, st.raw[P], bop);
-  v8i aops[NR][F::kMfmas];
-  load_aop<PACK, NR>(lc, gc, aops);
-  // the next group's bytes (past the stage's last group: the row padding, ignored)
-  if constexpr (P == 0) read_group_bytes<PACK, 1>(lc, bo, st.raw[1]);
-  else read_group_bytes<PACK, 0>(lc, bo + 2 * F::kGroupBytes, st.raw[0]);
-  float ccur[NR];
-  group_consts<PACK, NR, P>(sm, lc, sq0, gc, ccur, yacc);
-  v4f cur[NR];
-  group_mma<PACK, NR>(aops, bop, cur);
-  group_epilogue<NR>(st.prev, st.cprev, yacc);
+// The lane's two code dwords of group G (G may be the stage's group count:
+// the row padding is then read, in bounds, and never used).
+template <int G>
+__device__ __forceinline__ void read_group_codes(const StageBase& sb, uint32_t (&raw)[2]) {
+  const u32x2 w = lds_read<u32x2, 32 * G>(sb.row);
+  raw[0] = w.x;
+  raw[1] = w.y;
+}
+
+// B operand of a group: the 2-bit codes already are e2m1 nibbles for c/2;
+// even and odd codes of each dword go to separate dwords.
+__device__ __forceinline__ v8i make_bop2(const uint32_t (&raw)[2]) {
+  const uint32_t m = 0x33333333u;
+  return v8i{int(raw[0] & m), int((raw[0] >> 2) & m), int(raw[1] & m), int((raw[1] >> 2) & m), 0, 0, 0, 0};
+}
+
+// A operands of group G of the stage (lane rows of unused (batch, limb) pairs
+// read a valid limb row: row i of A only feeds row i of the result, never
+// stored).
+template <int NR, int G>
+__device__ __forceinline__ void load_aop(const StageBase& sb, v8i (&aops)[NR]) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
+    const u32x4 lo = lds_read<u32x4, G * kAGroup>(sb.a[r]), hi = lds_read<u32x4, G * kAGroup + 64>(sb.a[r]);
+    aops[r] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+  }
+}
+
+template <int NR>
+__device__ __forceinline__ void group_mma(const v8i (&aops)[NR], const v8i& bop, v4f (&out)[NR]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    out[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aops[r], bop, v4f{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0,
+                                                              127);
+}
+
+// y += s 2^-sig (2 (d0 + d1/16 + d2/256) - S) for group G, with d the limb
+// rows of this lane's result (batch 4r + q), the nibbles holding c/2 (hence
+// the doubling), S the activation sum and s the group's fp16 scale, half
+// G & 1 of sq[G / 2] (the stage's scales of the lane's row, two per dword).
+// Lanes of batches >= nb accumulate values that are never stored.  No branch
+// here on purpose: a matrix instruction must run with the whole wave active,
+// so its result may not feed a lane-divergent block.
+template <int NR, int G>
+__device__ __forceinline__ void group_epilogue(const v4f (&acc)[NR], const float2 (&fs)[NR], const uint32_t (&sq)[4],
+                                               float (&yacc)[NR]) {
+  const float sc = float(__builtin_bit_cast(_Float16, uint16_t((G & 1) ? sq[G >> 1] >> 16 : sq[G >> 1] & 0xFFFFu)));
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float p = fmaf(fmaf(acc[r][2], 0.00390625f, fmaf(acc[r][1], 0.0625f, acc[r][0])), 2.f, -fs[r].y);
+    yacc[r] = fmaf(sc, p * fs[r].x, yacc[r]);
+  }
+}
+
+// Pipeline state of one stage's group sequence.
+template <int NR>
+struct GroupPipe {
+  uint32_t raw[2][2];  // code dwords of the next group, by parity
+  v4f prev[NR];        // matrix results of the previous group
+};
+
+// Group G of a stage: B operand from codes read one step earlier, A
+// operands, the next group's codes and the previous group's factors, the
+// matrix instruction, then the previous group's epilogue (its matrix
+// results have had a whole step to arrive).
+template <int NR, int G>
+__device__ __forceinline__ void group_step(const StageBase& sb, const uint32_t (&sq)[4], GroupPipe<NR>& st,
+                                           float (&yacc)[NR]) {
+  constexpr int P = G & 1;
+  // the LDS reads stay in their step (not sunk to their use in the next)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  const v8i bop = make_bop2(st.raw[P]);
+  v8i aops[NR];
+  load_aop<NR, G>(sb, aops);
+  read_group_codes<G + 1>(sb, st.raw[P ^ 1]);
+  float2 fs[NR];
+  if constexpr (G > 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) fs[r] = lds_f2<8 * (G - 1)>(sb.f[r]);
+  }
+  v4f cur[NR];
+  group_mma<NR>(aops, bop, cur);
+  if constexpr (G > 0) group_epilogue<NR, G - 1>(st.prev, fs, sq, yacc);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) st.prev[r] = cur[r];
+  asm volatile("" ::: "memory");
+}
+
+// Groups G .. sg - 1 of a stage, unrolled (sg = 8 for full stages, where
+// every guard folds away; the launch's last stage may have fewer).
+template <int NR, int G>
+__device__ __forceinline__ void stage_groups(const StageBase& sb, int sg, const uint32_t (&sq)[4], GroupPipe<NR>& st,
+                                             float (&yacc)[NR]) {
+  if constexpr (G < kStageGroups) {
+    if (G < sg) {
+      group_step<NR, G>(sb, sq, st, yacc);
+      stage_groups<NR, G + 1>(sb, sg, sq, st, yacc);
+    } else if constexpr (G > 0) {
+      // the last group's epilogue
+      float2 fs[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) fs[r] = lds_f2<8 * (G - 1)>(sb.f[r]);
+      group_epilogue<NR, G - 1>(st.prev, fs, sq, yacc);
+    }
+  } else {
+    float2 fs[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) fs[r] = lds_f2<8 * (kStageGroups - 1)>(sb.f[r]);
+    group_epilogue<NR, kStageGroups - 1>(st.prev, fs, sq, yacc);
+  }
+}
+
+// ---- base-3, rolled group loop: two groups per iteration, each group's
+// table lookups made in its own step (the compute of a base-3 group is bound
+// by its LDS instructions, which unrolling does not reduce; rolled, two
+// stages of loads fit in registers).
+
+// Raw staged bytes of a group of parity P from bo (the group pair's start in
+// the lane's staged row): the dword pair holding bytes 6q .. 6q + 5 (a group
+// starts 2-byte aligned) and the dword holding bytes 24 and 25.
+template <int P>
+__device__ __forceinline__ void b3r_read_bytes(const LaneCtx& lc, uint32_t bo, uint32_t (&raw)[4]) {
+  const uint32_t a = bo + lc.b3_off[P];
+  raw[0] = lds_read<uint32_t>(a);
+  raw[1] = lds_read<uint32_t, 4>(a);
+  raw[2] = lds_read<uint32_t, P ? 48 : 24>(bo);
+  raw[3] = 0;
+}
+
+// B operand of a base-3 group of parity P: one lookup per byte in the plain
+// table (its five trits as nibbles 0..4 of a dword), shifted and ORed into
+// 32 dense nibbles: bytes 6q .. 6q + 5 in slots 0..29 and two of the ten
+// trits of bytes 24, 25 in slots 30, 31.
+template <int P>
+__device__ __forceinline__ v8i b3r_make_bop(const LaneCtx& lc, const uint32_t (&raw)[4]) {
+  const uint32_t sh = lc.b3_sh[P];
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);
+  const uint32_t w1 = raw[1] >> (8 * sh);
+  auto look = [&](uint32_t w, int byte) -> uint32_t {
+    // address bytes: [0] = lane copy offset, [1] = the code byte, [2..3] = 0
+    return lds_read<uint32_t>(__builtin_amdgcn_perm(lc.tab, w, 0x0C0C0004u | (uint32_t(byte) << 8)));
+  };
+  const uint32_t e0 = look(w0, 0), e1 = look(w0, 1), e2 = look(w0, 2), e3 = look(w0, 3);
+  const uint32_t e4 = look(w1, 0), e5 = look(w1, 1);
+  // bytes 24 and 25: byte 0 and 1 (even group) or 2 and 3 (odd group) of raw[2]
+  const uint32_t e24 = look(raw[2], P ? 2 : 0), e25 = look(raw[2], P ? 3 : 1);
+  const uint32_t extra = ((e24 | (e25 << 20)) >> lc.q8) & 0xFFu;
+  return v8i{int(e0 | (e1 << 20)), int((e1 >> 12) | (e2 << 8) | (e3 << 28)), int((e3 >> 4) | (e4 << 16)),
+             int((e4 >> 16) | (e5 << 4) | (extra << 24)), 0, 0, 0, 0};
+}
+
+// A operands of group gc of the launch.
+template <int NR>
+__device__ __forceinline__ void b3r_load_aop(const LaneCtx& lc, int gc, v8i (&aops)[NR]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t ag = uint32_t(lc.a_lane[r] + gc * kAGroup);
+    const u32x4 lo = lds_read<u32x4, 0>(ag), hi = lds_read<u32x4, 64>(ag);
+    aops[r] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+  }
+}
+
+// Pipeline state of a stage's rolled group loop.
+template <int NR>
+struct B3Pipe {
+  uint32_t raw[2][4];  // staged bytes of the next groups, by parity
+  v4f prev[NR];        // matrix results of the previous group
+  float cprev[NR];     // its epilogue factor s 2^-sig
+};
+
+// One group gc of parity P: B operand from bytes read one group earlier, the
+// A operands and epilogue factor, the next group's bytes, the matrix
+// instruction, then the previous group's epilogue.  So every dependent LDS
+// round trip except the table lookup is a group ahead of its use.  The
+// group's fp16 scale is half P of sq0.
+template <int NR, int P>
+__device__ __forceinline__ void b3r_group_step(const Smem& sm, const LaneCtx& lc, uint32_t bo, int gc, uint32_t sq0,
+                                               B3Pipe<NR>& st, float (&yacc)[NR]) {
+  __builtin_amdgcn_sched_barrier(0);
+  const v8i bop = b3r_make_bop<P>(lc, st.raw[P]);
+  v8i aops[NR];
+  b3r_load_aop<NR>(lc, gc, aops);
+  // the next group's bytes (past the stage's last group: the row padding, ignored)
+  if constexpr (P == 0) b3r_read_bytes<1>(lc, bo, st.raw[1]);
+  else b3r_read_bytes<0>(lc, bo + 2 * kB3GroupBytes, st.raw[0]);
+  const float sc = float(__builtin_bit_cast(_Float16, uint16_t(P ? sq0 >> 16 : sq0 & 0xFFFFu)));
+  float ccur[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) ccur[r] = sc * sm.f[lc.f_lane[r] + gc].x;
+  v4f cur[NR];
+  group_mma<NR>(aops, bop, cur);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    yacc[r] = fmaf(st.cprev[r], fmaf(st.prev[r][2], 0.00390625f, fmaf(st.prev[r][1], 0.0625f, st.prev[r][0])), yacc[r]);
     st.prev[r] = cur[r];
     st.cprev[r] = ccur[r];
   }
 }
 
-// All groups of one staged block of sg (1..8) groups, two per iteration of a
-// rolled loop (unrolled further, the compiler hoists later groups' loads and
-// runs out of registers).
-template <int PACK, int NR>
-__device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg,
-                                              int gc0, const uint32_t (&sreg)[4], float (&yacc)[NR]) {
-  using F = Fmt<PACK>;
-  GroupPipe<PACK, NR> st;
+// All groups of one staged block of sg (1..8) base-3 groups starting at group
+// gc0 of the launch, two per iteration of a rolled loop.
+template <int NR>
+__device__ __forceinline__ void b3r_stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg, int gc0,
+                                                  const uint32_t (&sreg)[4], float (&yacc)[NR]) {
+  B3Pipe<NR> st;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     st.prev[r] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -578,19 +649,47 @@ __device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, co
   }
   uint32_t sq[4] = {sreg[0], sreg[1], sreg[2], sreg[3]};
   uint32_t bo = stage + lc.b_row;
-  read_group_bytes<PACK, 0>(lc, bo, st.raw[0]);
+  b3r_read_bytes<0>(lc, bo, st.raw[0]);
   int g = 0;
 #pragma unroll 1
   for (; g + 1 < sg; g += 2) {
-    group_step<PACK, NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
-    group_step<PACK, NR, 1>(sm, lc, bo, gc0 + g + 1, sq[0], st, yacc);
-    bo += 2 * F::kGroupBytes;
+    b3r_group_step<NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
+    b3r_group_step<NR, 1>(sm, lc, bo, gc0 + g + 1, sq[0], st, yacc);
+    bo += 2 * kB3GroupBytes;
     sq[0] = sq[1];
     sq[1] = sq[2];
     sq[2] = sq[3];
   }
-  if (g < sg) group_step<PACK, NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
-  group_epilogue<NR>(st.prev, st.cprev, yacc);
+  if (g < sg) b3r_group_step<NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    yacc[r] = fmaf(st.cprev[r], fmaf(st.prev[r][2], 0.00390625f, fmaf(st.prev[r][1], 0.0625f, st.prev[r][0])), yacc[r]);
+}
+
+// All groups of one staged block of sg (1..8) groups starting at group gc0
+// of the launch.
+template <int PACK, int NR>
+__device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg,
+                                              int gc0, const uint32_t (&sreg)[4], float (&yacc)[NR]) {
+  if constexpr (PACK == 1) {
+    b3r_stage_compute<NR>(sm, stage, lc, sg, gc0, sreg, yacc);
+    return;
+  }
+  StageBase sb;
+  sb.row = stage + lc.b_row;
+  const uint32_t f0 = uint32_t(reinterpret_cast<uintptr_t>(sm.f) - reinterpret_cast<uintptr_t>(sm.lds));
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    sb.a[r] = uint32_t(lc.a_lane[r] + gc0 * kAGroup);
+    sb.f[r] = f0 + 8u * uint32_t(lc.f_lane[r] + gc0);
+  }
+  GroupPipe<NR> st;
+  read_group_codes<0>(sb, st.raw[0]);
+  // the group count stays opaque, so every group is its own basic block:
+  // within one block the compiler would gather the matrix instructions at
+  // the end and keep every group's operands alive until then
+  asm volatile("" : "+s"(sg));
+  stage_groups<NR, 0>(sb, sg, sreg, st, yacc);
 }
 
 // ---------------------------------------------------------------- streaming
@@ -598,7 +697,8 @@ __device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, co
 // Issue the loads of full stage s into registers.  Every lane issues every
 // load (a lane with nothing to load, or a stage past this wave's range, uses
 // an offset past the end of the buffer and reads zero), so the compiler
-// counts outstanding loads exactly and keeps kDepth stages in flight.
+// counts outstanding loads exactly and keeps every register slot's stage in
+// flight.
 template <int PACK, bool ALIGNED>
 __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t srs,
                                             const uint32_t (&src)[Fmt<PACK>::kLoads], uint32_t srow_scale,
@@ -640,8 +740,10 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One full stage: registers -> this wave's LDS buffer, matrix work, then
-// refill the same register slot with stage s + kDepth.
+// One full stage: registers -> this wave's LDS buffer, the matrix work, and
+// the refill of the register slot with stage s + kDepth (with one slot the
+// refill goes out before the matrix work, so a stage's loads are in flight
+// while the stage before it computes).
 template <int PACK, int NR, bool ALIGNED>
 __device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, uint32_t stage_addr, const LaneCtx& lc,
                                           __amdgpu_buffer_rsrc_t wrs,
@@ -665,8 +767,14 @@ __device__ __forceinline__ void run_stage(const Smem& sm, uint8_t* my_stage, uin
     }
   }
   wave_lds_fence();
-  stage_compute<PACK, NR>(sm, stage_addr, lc, kStageGroups, s * kStageGroups, sreg, yacc);
-  issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s + kDepth, s_end, regs, sreg);
+  if constexpr (F::kDepth == 1) {
+    const uint32_t sq[4] = {sreg[0], sreg[1], sreg[2], sreg[3]};
+    issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s + 1, s_end, regs, sreg);
+    stage_compute<PACK, NR>(sm, stage_addr, lc, kStageGroups, s * kStageGroups, sq, yacc);
+  } else {
+    stage_compute<PACK, NR>(sm, stage_addr, lc, kStageGroups, s * kStageGroups, sreg, yacc);
+    issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s + F::kDepth, s_end, regs, sreg);
+  }
 }
 
 // ---------------------------------------------------------------- kernel
@@ -711,7 +819,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   lc.b_row = nl * F::kRowLds + (PACK == 0 ? 8 * q : 0);
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
-    const int o = kB3GroupBytes * par + 6 * q;   // even: 0, 6, 12, 18; odd: 26, 32, 38, 44
+    const int o = kB3GroupBytes * par + 6 * q;  // even: 0, 6, 12, 18; odd: 26, 32, 38, 44
     lc.b3_off[par] = uint32_t(o & ~3);
     lc.b3_sh[par] = uint32_t(o & 3);
   }
@@ -784,15 +892,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   }
   const uint32_t srow_scale = row0 + nl < n ? uint32_t((row0 + nl) * groups + g_begin) : kNoLoad;
 
-  uint4 stg[kDepth][F::kLoads];
-  uint32_t scl[kDepth][4];
+  uint4 stg[F::kDepth][F::kLoads];
+  uint32_t scl[F::kDepth][4];
   if (prep) {
     if (PACK == 1 && !tab_by_rest) {
       for (int e = tid; e < 256; e += 64 * prep_waves) {
-        const uint32_t v = base3_t_nibbles(uint32_t(e));
-        uint4* dst = reinterpret_cast<uint4*>(sm.lds + 256 * e);
-#pragma unroll
-        for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
+        write_b3_entry(sm.lds, uint32_t(e));
       }
     }
     if constexpr (ROT) {
@@ -838,16 +943,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     // the table comes before this wave's weight loads: the loads would delay
     // it (it gates every wave's matrix work) more than it delays them
     for (int e = tid - 64 * prep_waves; e < 256; e += 64 * (nwaves - prep_waves)) {
-      const uint32_t v = base3_t_nibbles(uint32_t(e));
-      uint4* dst = reinterpret_cast<uint4*>(sm.lds + 256 * e);
-#pragma unroll
-      for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
+      write_b3_entry(sm.lds, uint32_t(e));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the table writes come before the count
     if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
+  for (int d = 0; d < F::kDepth; ++d)
     issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s_lo + d, s_full, stg[d], scl[d]);
   // every prep wave (and table wave) has finished (each adds 1 exactly once,
   // and none waits on anything, so this ends)
@@ -861,14 +963,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
 
   // ---- full stages, kDepth at a time so every register slot index is static
   int s = s_lo;
-  for (; s + kDepth <= s_full; s += kDepth) {
+  for (; s + F::kDepth <= s_full; s += F::kDepth) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d)
+    for (int d = 0; d < F::kDepth; ++d)
       run_stage<PACK, NR, ALIGNED>(sm, my_stage, my_stage_addr, lc, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d],
                                    scl[d], yacc);
   }
 #pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d)
+  for (int d = 0; d < F::kDepth - 1; ++d)
     if (s + d < s_full)
       run_stage<PACK, NR, ALIGNED>(sm, my_stage, my_stage_addr, lc, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d],
                                    scl[d], yacc);
