@@ -89,9 +89,14 @@ __host__ __device__ constexpr int a_batch_stride(int ng, int mfmas) {
   const int base = ng * mfmas * kAGroup;
   return base + (48 - base % 128 + 128) % 128;
 }
-// Bytes of the per-(batch, group) factor region, rounded to 16, plus 16 for
-// the workgroup's ready counter.
-__host__ __device__ constexpr int f_region_bytes(int nb, int ng) { return ((nb * ng * 8 + 15) & ~15) + 16; }
+// Bytes of the per-(batch, group) factor region: the factors, then one
+// exponent byte per (batch, group), each rounded to 16, plus 16 for the
+// workgroup's ready counter.
+__host__ __device__ constexpr int f_bytes(int nb, int ng) { return (nb * ng * 8 + 15) & ~15; }
+__host__ __device__ constexpr int e0_stride(int ng) { return (ng + 7) & ~7; }  // 8-byte aligned rows
+__host__ __device__ constexpr int f_region_bytes(int nb, int ng) {
+  return f_bytes(nb, ng) + ((nb * e0_stride(ng) + 15) & ~15) + 16;
+}
 
 // K-slot of trit tau (0..127) of a group, and which matrix instruction of the
 // group it belongs to.  B operand: lane group q supplies slots 32q..32q+31.
@@ -130,6 +135,7 @@ struct Smem {
   uint8_t* a;       // [B][ng][mfmas][3][144] activation limbs in K-slot order
   int a_bstride;    // bytes between batches in a
   float2* f;        // [B][ng] = {2^-sig, sum of reconstructed activations}
+  uint8_t* e0;      // [B][e0_stride(ng)] = 127 - sig, the E8M0 exponent of limb 0 (after f)
   int ng;           // groups of this launch
   int* ready;       // count of prep waves done (after f)
   uint8_t* stage;   // waves x kStageLds (reused for the K-part reduction at the end)
@@ -169,6 +175,7 @@ __device__ __forceinline__ void write_b3_entry(uint8_t* lds, uint32_t e) {
   uint4* dst = reinterpret_cast<uint4*>(lds + 256 * e);
 #pragma unroll
   for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
+
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -354,7 +361,11 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
   if (mx > 0.f) {
     int ex;
     frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
-    sig = 8 - ex;     // mx * 2^sig in [128, 256)
+    // mx * 2^sig in [128, 256), kept within [-127, 119] so that every limb
+    // exponent 127 - sig - 4 limb is a valid E8M0 value.  Only a group whose
+    // maximum is below 2^-111 is scaled less; its elements keep full limb
+    // precision down to about 2^-125, so only fp32 subnormals are affected.
+    sig = min(max(8 - ex, -127), 119);
   }
   float cur[10];
 #pragma unroll
@@ -403,7 +414,10 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
     }
   }
   if constexpr (PACK == 0) sum = row16_sum(sum);  // only the 2-bit path needs it
-  if (l16 == 0) sm.f[b * sm.ng + g] = make_float2(ldexpf(1.f, -sig), sum);
+  if (l16 == 0) {
+    sm.f[b * sm.ng + g] = make_float2(ldexpf(1.f, -sig), sum);
+    sm.e0[b * e0_stride(sm.ng) + g] = uint8_t(127 - sig);
+  }
 }
 
 // ---------------------------------------------------------------- matrix work
@@ -419,6 +433,9 @@ struct LaneCtx {
   // within it (0 or 2)
   uint32_t b3_off[2], b3_sh[2];
   uint32_t q8;    // 8 * lane group: which two of the ten extra trits are this lane's
+  // base-3, per row set: LDS address of the e0 row of this lane's A-row
+  // batch, and 4 * its limb in every byte (the limb's exponent offset)
+  uint32_t e_lane[2], e_limb;
 };
 
 // A float2 from LDS (vector types have no address-space-qualified copy).
@@ -604,17 +621,20 @@ template <int NR>
 struct B3Pipe {
   uint32_t raw[2][4];  // staged bytes of the next groups, by parity
   v4f prev[NR];        // matrix results of the previous group
-  float cprev[NR];     // its epilogue factor s 2^-sig
+  float sprev;         // its fp16 weight scale
+  uint32_t ex[NR][2];  // E8M0 exponents of this lane's A row for the stage's next groups, one a byte
 };
 
 // One group gc of parity P: B operand from bytes read one group earlier, the
-// A operands and epilogue factor, the next group's bytes, the matrix
-// instruction, then the previous group's epilogue.  So every dependent LDS
-// round trip except the table lookup is a group ahead of its use.  The
-// group's fp16 scale is half P of sq0.
+// A operands, the next group's bytes, the matrix instruction, then the
+// previous group's epilogue.  So every dependent LDS round trip except the
+// table lookup is a group ahead of its use.  The matrix instruction scales
+// A row (batch, limb) by 2^-sig 16^-limb through its E8M0 scale (byte P of
+// ex[r][0]), so a result is just s (d0 + d1 + d2); the group's fp16 scale s
+// is half P of sq0.
 template <int NR, int P>
-__device__ __forceinline__ void b3r_group_step(const Smem& sm, const LaneCtx& lc, uint32_t bo, int gc, uint32_t sq0,
-                                               B3Pipe<NR>& st, float (&yacc)[NR]) {
+__device__ __forceinline__ void b3r_group_step(const LaneCtx& lc, uint32_t bo, int gc, uint32_t sq0, B3Pipe<NR>& st,
+                                               float (&yacc)[NR]) {
   __builtin_amdgcn_sched_barrier(0);
   const v8i bop = b3r_make_bop<P>(lc, st.raw[P]);
   v8i aops[NR];
@@ -623,47 +643,56 @@ __device__ __forceinline__ void b3r_group_step(const Smem& sm, const LaneCtx& lc
   if constexpr (P == 0) b3r_read_bytes<1>(lc, bo, st.raw[1]);
   else b3r_read_bytes<0>(lc, bo + 2 * kB3GroupBytes, st.raw[0]);
   const float sc = float(__builtin_bit_cast(_Float16, uint16_t(P ? sq0 >> 16 : sq0 & 0xFFFFu)));
-  float ccur[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) ccur[r] = sc * sm.f[lc.f_lane[r] + gc].x;
   v4f cur[NR];
-  group_mma<NR>(aops, bop, cur);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    cur[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aops[r], bop, v4f{0.f, 0.f, 0.f, 0.f}, 0, 4, P,
+                                                              int(st.ex[r][0]), 0, 127);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    yacc[r] = fmaf(st.cprev[r], fmaf(st.prev[r][2], 0.00390625f, fmaf(st.prev[r][1], 0.0625f, st.prev[r][0])), yacc[r]);
+    yacc[r] = fmaf(st.sprev, st.prev[r][0] + st.prev[r][1] + st.prev[r][2], yacc[r]);
     st.prev[r] = cur[r];
-    st.cprev[r] = ccur[r];
   }
+  st.sprev = sc;
 }
 
 // All groups of one staged block of sg (1..8) base-3 groups starting at group
 // gc0 of the launch, two per iteration of a rolled loop.
 template <int NR>
-__device__ __forceinline__ void b3r_stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg, int gc0,
+__device__ __forceinline__ void b3r_stage_compute(uint32_t stage, const LaneCtx& lc, int sg, int gc0,
                                                   const uint32_t (&sreg)[4], float (&yacc)[NR]) {
   B3Pipe<NR> st;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     st.prev[r] = v4f{0.f, 0.f, 0.f, 0.f};
-    st.cprev[r] = 0.f;
+    // the stage's eight limb-0 exponents of this lane's batch, less 4 limb
+    // (no byte borrows: 127 - sig >= 8)
+    const uint32_t e = lc.e_lane[r] + uint32_t(gc0);
+    st.ex[r][0] = lds_read<uint32_t>(e) - lc.e_limb;
+    st.ex[r][1] = lds_read<uint32_t, 4>(e) - lc.e_limb;
   }
+  st.sprev = 0.f;
   uint32_t sq[4] = {sreg[0], sreg[1], sreg[2], sreg[3]};
   uint32_t bo = stage + lc.b_row;
   b3r_read_bytes<0>(lc, bo, st.raw[0]);
   int g = 0;
 #pragma unroll 1
   for (; g + 1 < sg; g += 2) {
-    b3r_group_step<NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
-    b3r_group_step<NR, 1>(sm, lc, bo, gc0 + g + 1, sq[0], st, yacc);
+    b3r_group_step<NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
+    b3r_group_step<NR, 1>(lc, bo, gc0 + g + 1, sq[0], st, yacc);
     bo += 2 * kB3GroupBytes;
     sq[0] = sq[1];
     sq[1] = sq[2];
     sq[2] = sq[3];
-  }
-  if (g < sg) b3r_group_step<NR, 0>(sm, lc, bo, gc0 + g, sq[0], st, yacc);
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
-    yacc[r] = fmaf(st.cprev[r], fmaf(st.prev[r][2], 0.00390625f, fmaf(st.prev[r][1], 0.0625f, st.prev[r][0])), yacc[r]);
+    for (int r = 0; r < NR; ++r) {
+      st.ex[r][0] = __builtin_amdgcn_alignbyte(st.ex[r][1], st.ex[r][0], 2);
+      st.ex[r][1] >>= 16;
+    }
+  }
+  if (g < sg) b3r_group_step<NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) yacc[r] = fmaf(st.sprev, st.prev[r][0] + st.prev[r][1] + st.prev[r][2], yacc[r]);
 }
 
 // All groups of one staged block of sg (1..8) groups starting at group gc0
@@ -672,7 +701,7 @@ template <int PACK, int NR>
 __device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg,
                                               int gc0, const uint32_t (&sreg)[4], float (&yacc)[NR]) {
   if constexpr (PACK == 1) {
-    b3r_stage_compute<NR>(sm, stage, lc, sg, gc0, sreg, yacc);
+    b3r_stage_compute<NR>(stage, lc, sg, gc0, sreg, yacc);
     return;
   }
   StageBase sb;
@@ -810,6 +839,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   sm.a_bstride = a_batch_stride(ng, F::kMfmas);
   const int a_bytes = nb * sm.a_bstride;
   sm.f = reinterpret_cast<float2*>(sm.a + a_bytes);
+  sm.e0 = sm.a + a_bytes + f_bytes(nb, ng);
   sm.ng = ng;
   sm.ready = reinterpret_cast<int*>(sm.a + a_bytes + f_region_bytes(nb, ng) - 16);
   sm.stage = sm.a + a_bytes + f_region_bytes(nb, ng);
@@ -824,12 +854,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     lc.b3_sh[par] = uint32_t(o & 3);
   }
   lc.q8 = uint32_t(8 * q);
+  lc.e_limb = uint32_t(4 * min(nl & 3, 2)) * 0x01010101u;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     // A rows are 4b + limb; unused rows (limb 3, or batch >= nb) read a valid
     // limb row instead (they only feed result rows that are never read)
     const int limb = min(nl & 3, 2), b = min(4 * r + (nl >> 2), nb - 1);
     lc.a_lane[r] = F::kTable + b * sm.a_bstride + limb * kARow + 16 * q;
+    lc.e_lane[r] = uint32_t(F::kTable + a_bytes + f_bytes(nb, ng) + b * e0_stride(ng));
     lc.f_lane[r] = min(4 * r + q, nb - 1) * ng;
   }
   lc.tab = uint32_t(4 * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
@@ -1040,7 +1072,7 @@ Plan make_plan(int b, int n, int k) {
   using F = Fmt<PACK>;
   const int tiles = (n + 15) / 16;
   const int groups = k / kGroup;
-  const int per_group = F::kMfmas * b * kAGroup + b * 8;  // + b * 127 bytes of batch padding
+  const int per_group = F::kMfmas * b * kAGroup + b * 9;  // + b * 127 bytes of batch padding, b * 7 of e0 rows
   // smallest tiles-per-workgroup that keeps the grid within one workgroup per CU
   int rt = 1;
   while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
@@ -1050,7 +1082,7 @@ Plan make_plan(int b, int n, int k) {
   int ks = kMaxWaves / rt, ng = 0;
   for (; ks >= 1; --ks) {
     const int extra = ROT ? rot_extra<PACK>(rt * ks, 1 << 20) : 0;
-    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 127 - 31 - extra;
+    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 134 - 46 - extra;
     ng = room > 0 ? room / per_group : 0;
     if (ng >= kStageGroups || ks == 1) break;
   }
