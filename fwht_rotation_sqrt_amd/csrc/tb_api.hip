@@ -92,8 +92,13 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
   if (N == 0) return TB_OK;
   if (!packed || !scales || !xr || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr) || !aligned16(y)) return TB_ERR_ALIGN;
-  tb::launch_gemv(packing, packed, scales, xr, xr_dtype, y, int(B), int(N), int(K),
-                  static_cast<hipStream_t>(stream));
+  // batches above the kernel's row sets run as chunks of rows
+  const size_t xsz = xr_dtype == TB_F32 ? 4 : 2;
+  for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
+    const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;
+    tb::launch_gemv(packing, packed, scales, static_cast<const uint8_t*>(xr) + size_t(b0) * size_t(K) * xsz,
+                    xr_dtype, y + b0 * N, int(bc), int(N), int(K), static_cast<hipStream_t>(stream));
+  }
   return finish_launch();
 }
 
@@ -107,8 +112,12 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
   if (!packed || !scales || !x || !sign_bits || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y))
     return TB_ERR_ALIGN;
-  tb::launch_linear(packing, packed, scales, x, x_dtype, sign_bits, y, int(B), int(N), int(K),
-                    static_cast<hipStream_t>(stream));
+  const size_t xsz = x_dtype == TB_F32 ? 4 : 2;
+  for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
+    const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;
+    tb::launch_linear(packing, packed, scales, static_cast<const uint8_t*>(x) + size_t(b0) * size_t(K) * xsz,
+                      x_dtype, sign_bits, y + b0 * N, int(bc), int(N), int(K), static_cast<hipStream_t>(stream));
+  }
   return finish_launch();
 }
 

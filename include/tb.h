@@ -49,8 +49,11 @@ typedef enum {
 typedef enum { TB_PACK_2BIT = 0, TB_PACK_BASE3 = 1 } tb_packing;
 typedef enum { TB_F32 = 0, TB_F16 = 1, TB_BF16 = 2 } tb_dtype;
 
-/* Largest batch tb_gemv accepts. */
-#define TB_GEMV_MAX_BATCH 8
+/* Largest batch tb_gemv and tb_linear accept.  Up to TB_GEMV_KERNEL_BATCH
+ * rows run in one pass over the weights; a larger batch runs in chunks of
+ * TB_GEMV_KERNEL_BATCH rows, each streaming the weights again. */
+#define TB_GEMV_MAX_BATCH 32
+#define TB_GEMV_KERNEL_BATCH 8
 
 /* Bytes of one packed row of K weights: K/4 for 2-bit codes, 26*K/128 for
  * base-3 codes; -1 if K is negative or not a multiple of 128 or the packing
@@ -107,7 +110,8 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
  * weight bytes streamed per token).
  * packed: [N][tb_packed_row_bytes(packing, K)]; scales: fp16 [N][K/128];
  * xr: [B][K] rotated activations of xr_dtype (TB_F32 or TB_F16), read as
- * given; y: fp32 [B][N], overwritten.  1 <= B <= TB_GEMV_MAX_BATCH.
+ * given; y: fp32 [B][N], overwritten.  1 <= B <= TB_GEMV_MAX_BATCH (above
+ * TB_GEMV_KERNEL_BATCH in chunks, see there).
  * Accumulation is fp32 (not bit-reproducible across kernel versions). */
 int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
             int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, void* stream);
@@ -121,7 +125,7 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
  * besides the product).
  * x: [B][K] unrotated activations of x_dtype (TB_F32, TB_F16 or TB_BF16);
  * sign_bits, packed, scales and y as for tb_fwht_rotate and tb_gemv.
- * K % 1024 == 0; 1 <= B <= TB_GEMV_MAX_BATCH.  x' is kept in fp32 inside the
+ * K % 1024 == 0; 1 <= B <= TB_GEMV_MAX_BATCH (chunked as tb_gemv).  x' is kept in fp32 inside the
  * call (never rounded to fp16), so the result matches tb_fwht_rotate to fp32
  * followed by tb_gemv to fp32 accumulation order. */
 int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,

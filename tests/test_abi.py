@@ -83,7 +83,7 @@ def test_gemv_validation():
     g = lib.tb_gemv
     assert g(3, P, P, P, 0, P, 1, 8, 128, None) == UNSUP
     assert g(0, P, P, P, 0, P, 0, 8, 128, None) == SHAPE
-    assert g(0, P, P, P, 0, P, 9, 8, 128, None) == SHAPE
+    assert g(0, P, P, P, 0, P, tb.TB_GEMV_MAX_BATCH + 1, 8, 128, None) == SHAPE
     assert g(0, P, P, P, 0, P, 1, 8, 192, None) == SHAPE
     assert g(0, P, P, P, 0, P, 1, -8, 128, None) == SHAPE
     assert g(0, P, P, P, 2, P, 1, 8, 128, None) == DTYPE
@@ -101,7 +101,7 @@ def test_linear_validation():
     # (packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream)
     assert g(3, P, P, P, 2, P, P, 1, 8, 1024, None) == UNSUP
     assert g(1, P, P, P, 2, P, P, 0, 8, 1024, None) == SHAPE
-    assert g(1, P, P, P, 2, P, P, 9, 8, 1024, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, tb.TB_GEMV_MAX_BATCH + 1, 8, 1024, None) == SHAPE
     assert g(1, P, P, P, 2, P, P, 1, 8, 1152, None) == SHAPE      # K % 1024 != 0
     assert g(1, P, P, P, 2, P, P, 1, -8, 1024, None) == SHAPE
     assert g(1, P, P, P, 3, P, P, 1, 8, 1024, None) == DTYPE

@@ -212,6 +212,60 @@ def test_linear_fused_rotation(packing, n, k, x_dtype):
         assert oracle.rel_err(got, want[:b]) < TOL, b
 
 
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("exp2", [-120, 100])
+def test_gemv_extreme_magnitudes(packing, exp2):
+    """Activations scaled by 2^exp2 (exactly).  At 2^-120 every group's
+    power-of-two scale hits its upper clamp (the limb exponents must stay
+    valid E8M0 values); at 2^100 the scale is far negative.  The error bound
+    is relative to the row rms, so it is the same at any scale."""
+    n, k = 300, 5120
+    note(f"gemv/linear {packing} x * 2^{exp2}")
+    g = synth.rng(250, 0, exp2 & 255, 0)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x32 = np.ldexp(g.standard_normal((4, k)), exp2).astype(np.float32)
+    assert np.all(np.isfinite(x32)) and np.min(np.abs(x32[x32 != 0])) > 0
+    x64 = x32.astype(np.float64)
+    packed, _ = PACK_REF[packing](t)
+    pd, sd, xd = dev(packed), scales_dev(s), dev(x32)
+    # x' given: the exact rotation of the fp32 activations, rounded to fp32
+    xr = oracle.rotate(x64, signs)
+    want = oracle.gemv(packing, packed, s, xr, k)
+    got = host(tb.tb_gemv(packing, pd, sd, dev(xr.astype(np.float32))))
+    assert oracle.rel_err(got, want) < TOL
+    # rotation fused
+    got = host(tb.tb_linear(packing, pd, sd, xd, signs_dev(signs)))
+    assert oracle.rel_err(got, want) < TOL
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_gemv_linear_batches_above_8(packing):
+    """Batches above 8 run as chunks of 8 rows over the weights; every row
+    must match the oracle, across chunk boundaries and with a ragged last
+    chunk."""
+    n, k = 200, 3072
+    note(f"gemv/linear {packing} batches 9..32")
+    g = synth.rng(260, 0, 0, 0)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x32 = g.standard_normal((tb.TB_GEMV_MAX_BATCH, k)).astype(np.float32)
+    x64 = x32.astype(np.float64)
+    packed, _ = PACK_REF[packing](t)
+    xr = oracle.rotate(x64, signs)
+    want = oracle.gemv(packing, packed, s, xr, k)
+    pd, sd, sgn = dev(packed), scales_dev(s), signs_dev(signs)
+    xrd, xd = dev(xr.astype(np.float32)), dev(x32)
+    for b in (9, 16, 21, tb.TB_GEMV_MAX_BATCH):
+        got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
+        assert got.shape == (b, n)
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_gemv", b)
+        got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear", b)
+
+
 # ------------------------------------------------------------------ prefill product
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
