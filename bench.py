@@ -18,6 +18,12 @@ baseline.
 
 Prints one JSON line (rank 0).  `value` is the decode step's packed-weight
 stream rate in GB/s (codes + scales per step / step time).
+
+`--suite OUT.md` instead times every block linear (q/k/v/o 5120x5120,
+gate/up 17408x5120, down 5120x17408; both packings; batch 1 and 8), one
+decode token through 64 distinct base-3 layers (5.2 GB of weights; q/k/v and
+gate/up concatenated, so four calls per layer) with the rotation's share of
+the separate route, and plain torch streams, and writes a markdown summary.
 """
 from __future__ import annotations
 
@@ -50,6 +56,9 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating HBM byte counters) and exit")
+    ap.add_argument("--suite", metavar="OUT_MD",
+                    help="instead of the one-line record: time the block linears (both packings, batch 1 and 8), "
+                         "the 64-layer decode token stream and a 2 GiB read, and write a markdown summary")
     return ap.parse_args()
 
 
@@ -219,6 +228,213 @@ def cpu_baseline(d, budget_s=15.0):
             "sample": f"{runs} full passes of rotate+GEMV (17408x5120 base-3, batch 1) in fp64 numpy, {el:.1f} s"}
 
 
+# ---------------------------------------------------------------- --suite
+#
+# Weights for the suite are drawn on the GPU (torch's Philox generator, seeded
+# per tensor) with the same distributions as the seeded host generators: trits
+# P(0) = 0.5, P(+1) = P(-1) = 0.25; scales |N(0, 0.02)| + 1e-3 in fp16; bf16
+# N(0, 1) activations.  Timing does not depend on the values, and 24 G host
+# trits would take far too long to draw.
+
+SUITE_SEED = 0x7B500002
+
+
+def gpu_trits(n, k, gen):
+    r = torch.randint(0, 4, (n, k), dtype=torch.int8, device="cuda", generator=gen)
+    return (r == 3).to(torch.int8) - (r == 0).to(torch.int8)
+
+
+def gpu_scales(n, k, gen):
+    return (torch.randn((n, k // 128), device="cuda", generator=gen) * 0.02).abs_().add_(1e-3).half()
+
+
+def gpu_packed(packing, n, k, gen):
+    t = gpu_trits(n, k, gen)
+    p = (tb.tb_pack_2bit if packing == "2bit" else tb.tb_pack_base3)(t)
+    del t
+    return p, gpu_scales(n, k, gen)
+
+
+def gpu_signs(k):
+    return dev(synth.sign_bits(synth.rng(4, synth.T_SIGNS), k).view(np.int32))
+
+
+def suite_linear(packing, n, k, b, gen, steps=50):
+    """One linear at batch b: fused call, rotation alone, product alone; us per call."""
+    p0, s0 = gpu_packed(packing, n, k, gen)
+    per = p0.numel() + 2 * s0.numel()
+    copies = max(2, -(-CACHE_BYTES // per))
+    ps = [p0] + [p0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    x = torch.randn((b, k), device="cuda", generator=gen).to(torch.bfloat16)
+    sg = gpu_signs(k)
+    xr = torch.empty((b, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+
+    def fused():
+        for i in range(steps):
+            tb.tb_linear(packing, ps[i % copies], ss[i % copies], x, sg, y=y)
+
+    def rot():
+        for _ in range(steps):
+            tb.tb_fwht_rotate(x, sg, out=xr)
+
+    def gemv():
+        for i in range(steps):
+            tb.tb_gemv(packing, ps[i % copies], ss[i % copies], xr, y=y)
+
+    out = {}
+    for name, fn in (("fused", fused), ("rotate", rot), ("gemv", gemv)):
+        _, g = time_graph(fn, fn)
+        out[name] = event_time(g, 3) / steps * 1e6
+        del g
+    out["bytes"] = per
+    del ps, ss
+    return out
+
+
+def suite_token(gen, layers=64, reps=10):
+    """One decode token at batch 1 through 64 layers of base-3 linears, q/k/v and
+    gate/up concatenated (4 calls per layer): whole-token graph time, fused and
+    separate routes, and the rotation's share of the separate route."""
+    H, F = synth.HIDDEN, synth.FFN
+    shapes = (("qkv", 3 * H, H), ("o", H, H), ("gate_up", 2 * F, H), ("down", H, F))
+    W = []
+    total = 0
+    for _ in range(layers):
+        lw = []
+        for _, n, k in shapes:
+            p, s = gpu_packed("base3", n, k, gen)
+            total += p.numel() + 2 * s.numel()
+            x = torch.randn((1, k), device="cuda", generator=gen).to(torch.bfloat16)
+            lw.append((p, s, x))
+        W.append(lw)
+    sg = {H: gpu_signs(H), F: gpu_signs(F)}
+    xr = {H: torch.empty((1, H), dtype=torch.float32, device="cuda"),
+          F: torch.empty((1, F), dtype=torch.float32, device="cuda")}
+    ys = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n, _ in shapes]
+
+    def fused(only=None):
+        for lw in W:
+            for j, ((_, n, k), (p, s, x)) in enumerate(zip(shapes, lw)):
+                if only is None or only == j:
+                    tb.tb_linear("base3", p, s, x, sg[k], y=ys[j])
+
+    def separate(rot=True, prod=True):
+        for lw in W:
+            for j, ((_, n, k), (p, s, x)) in enumerate(zip(shapes, lw)):
+                if rot:
+                    tb.tb_fwht_rotate(x, sg[k], out=xr[k])
+                if prod:
+                    tb.tb_gemv("base3", p, s, xr[k], y=ys[j])
+
+    res = {"bytes": total, "layers": layers, "calls_fused": 4 * layers}
+    for name, fn in (("fused", fused), ("separate", separate),
+                     ("rotate_only", lambda: separate(True, False)), ("gemv_only", lambda: separate(False, True))):
+        _, g = time_graph(fn, fn)
+        res[name] = event_time(g, reps)
+        del g
+    for j, (nm, n, k) in enumerate(shapes):
+        _, g = time_graph(lambda j=j: fused(j), lambda j=j: fused(j))
+        res["call_" + nm] = (n, k, event_time(g, reps) / layers)
+        del g
+    del W
+    return res
+
+
+def suite_read_calibration(reps=10):
+    """Plain HBM streams through torch's own kernels: a 2 GiB read (sum over
+    fp32) and a 1 GiB copy (2 GiB moved).  A lower bound on what the box
+    streams; neither kernel is tuned for this."""
+    buf = torch.ones(512 << 20, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    half = buf[: 256 << 20]
+    dst = torch.empty_like(half)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_read = timed(lambda: out.copy_(buf.sum()))
+    t_copy = timed(lambda: dst.copy_(half))
+    del buf, dst
+    return {"read_us": t_read * 1e6, "gbs": (2 << 30) / t_read / 1e9,
+            "copy_us": t_copy * 1e6, "copy_gbs": (2 << 30) / t_copy / 1e9}
+
+
+def run_suite(path, argv):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(SUITE_SEED)
+    lines = []
+    cal = suite_read_calibration()
+    print(f"read calibration: {cal['gbs']:.0f} GB/s read, {cal['copy_gbs']:.0f} GB/s copy", flush=True)
+    rows = []
+    for packing in ("2bit", "base3"):
+        for b in (1, 8):
+            for lin in synth.BLOCK_LINEARS:
+                r = suite_linear(packing, lin.n, lin.k, b, gen)
+                rows.append((lin, packing, b, r))
+                print(f"{lin.name} {lin.n}x{lin.k} {packing} b{b}: fused {r['fused']:.2f} us, "
+                      f"rotate {r['rotate']:.2f} + gemv {r['gemv']:.2f} us", flush=True)
+    tok = suite_token(gen)
+    print(f"token: fused {tok['fused'] * 1e3:.3f} ms, separate {tok['separate'] * 1e3:.3f} ms", flush=True)
+
+    pk = HBM_PEAK_GBS
+    lines.append("# Block linears and the 64-layer decode token stream (MI355X, one GPU)")
+    lines.append("")
+    lines.append("Command: `python bench.py " + " ".join(argv) + "`")
+    lines.append("")
+    lines.append("Graph-replayed calls on cache-cold weights (each linear cycles through > 512 MB of copies; "
+                 "the token stream's 64 distinct layers hold "
+                 f"{tok['bytes'] / 1e9:.2f} GB). Weights drawn on the GPU (seed {SUITE_SEED:#x}); "
+                 "bf16 N(0,1) activations. GB/s counts packed codes + fp16 scales; % is of 8 TB/s.")
+    lines.append("")
+    lines.append(f"Plain streams through torch's own kernels (a lower bound on the box's rate): 2 GiB read "
+                 f"(sum over fp32) {cal['read_us']:.1f} us = {cal['gbs']:.0f} GB/s; 1 GiB copy (2 GiB moved) "
+                 f"{cal['copy_us']:.1f} us = {cal['copy_gbs']:.0f} GB/s.")
+    lines.append("")
+    lines.append("## Block linears (q/k/v/o 5120x5120, gate/up 17408x5120, down 5120x17408)")
+    lines.append("")
+    lines.append("| linear | N x K | packing | batch | MB | tb_linear us | GB/s | % peak | rotate us | tb_gemv us |")
+    lines.append("|---|---|---|---|---|---|---|---|---|---|")
+    for lin, packing, b, r in rows:
+        gbs = r["bytes"] / (r["fused"] * 1e-6) / 1e9
+        lines.append(f"| {lin.name} | {lin.n}x{lin.k} | {packing} | {b} | {r['bytes'] / 1e6:.2f} | {r['fused']:.2f} | "
+                     f"{gbs:.0f} | {100 * gbs / pk:.1f} | {r['rotate']:.2f} | {r['gemv']:.2f} |")
+    lines.append("")
+    lines.append("## Decode token stream: 64 layers, base-3, batch 1 (q/k/v and gate/up concatenated)")
+    lines.append("")
+    t_f, t_s, t_r, t_g = tok["fused"], tok["separate"], tok["rotate_only"], tok["gemv_only"]
+    lines.append(f"- Weight bytes per token: {tok['bytes']:,} ({tok['calls_fused']} product calls).")
+    lines.append(f"- Fused route (tb_linear, rotation in the prologue): {t_f * 1e3:.3f} ms per token = "
+                 f"**{1 / t_f:.1f} tokens/s-equivalent**, {tok['bytes'] / t_f / 1e9:.0f} GB/s "
+                 f"({100 * tok['bytes'] / t_f / 1e9 / pk:.1f} % of 8 TB/s).")
+    lines.append(f"- Separate route (tb_fwht_rotate to fp32, then tb_gemv): {t_s * 1e3:.3f} ms per token = "
+                 f"{1 / t_s:.1f} tokens/s-equivalent.")
+    lines.append(f"- Rotation alone (256 calls): {t_r * 1e3:.3f} ms; products alone: {t_g * 1e3:.3f} ms; "
+                 f"FWHT share of the separate route = {100 * t_r / (t_r + t_g):.1f} %.")
+    lines.append("")
+    lines.append("| call | N x K | us per call (fused) | GB/s |")
+    lines.append("|---|---|---|---|")
+    for nm in ("qkv", "o", "gate_up", "down"):
+        n, k, t = tok["call_" + nm]
+        byts = n * (tb.tb_packed_row_bytes("base3", k) + 2 * (k // 128))
+        lines.append(f"| {nm} | {n}x{k} | {t * 1e6:.2f} | {byts / t / 1e9:.0f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"suite": path, "token_ms_fused": round(t_f * 1e3, 4),
+                      "tokens_per_s_equiv": round(1 / t_f, 1), "read_calibration_gbs": round(cal["gbs"], 1)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,6 +452,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 5}), flush=True)
         return
     tb.library()
+    if args.suite:
+        run_suite(args.suite, sys.argv[1:])
+        return
     d = decode_setup()
     wall, t_fused, t_gemv, t_rot = bench_decode(d, args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3

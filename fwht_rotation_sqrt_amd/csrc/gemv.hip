@@ -866,31 +866,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   }
   lc.tab = uint32_t(4 * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
 
-  // ---- roles.  The first prep_waves waves build the activation limbs and
-  // only then load weights; the others (after the base-3 table, when they
-  // write it) start the weight stream at once.  A wave starts its matrix work when the LDS counter shows
-  // every prep wave done, not at a workgroup barrier, so it never waits for
-  // another wave's weight loads to be issued.
+  // ---- roles.  Waves 0 .. rt*ks - 1 own row tiles and stages (compute
+  // waves); a launch may add waves beyond them that only build limbs (more
+  // (batch, group) pairs than the compute waves' teams would cover in a few
+  // passes, as at batch 8).  Prep waves are taken in prep-rank order: the
+  // extra waves first, then compute waves 0, 1, ...  A compute wave that
+  // preps loads its weights only afterwards; the others (after the base-3
+  // table, when they write it) start the weight stream at once.  A wave
+  // starts its matrix work when the LDS counter shows every prep wave done,
+  // not at a workgroup barrier, so it never waits for another wave's weight
+  // loads to be issued.
   const int pairs = ng * nb;
-  const int nwaves = rt * ks;
+  const int ncomp = rt * ks;
+  const int nw = int(blockDim.x) >> 6;
+  const bool comp = wave < ncomp;
+  const int prank = comp ? wave + (nw - ncomp) : wave - ncomp;
   // rotation units: (batch, block) pairs, one wave each at a time
   const int nblk = ng / 8, units = nb * nblk;
-  const int prep_waves = ROT ? min(min(nwaves, units), kMaxRotWaves)
-                             : min(nwaves, (pairs + 11) / 12);  // ~3 (batch, group) pairs per team
-  const bool prep = wave < prep_waves;
-  const int team = tid / kTeam, l16 = tid % kTeam, nteams = prep_waves * (64 / kTeam);
+  const int prep_waves = ROT ? min(min(nw, units), kMaxRotWaves)
+                             : max(nw - ncomp, min(nw, (pairs + 11) / 12));  // ~3 (batch, group) pairs per team
+  const bool prep = prank < prep_waves;
+  const int team = prank * (64 / kTeam) + (lane >> 4), l16 = lane & (kTeam - 1), nteams = prep_waves * (64 / kTeam);
   // The base-3 decode table is written by the waves that build no limbs
   // (they would otherwise sit idle until the limbs are ready), or by the prep
   // waves when every wave is one.  Each table wave adds 1 to the ready count.
-  const bool tab_by_rest = PACK == 1 && nwaves > prep_waves;
-  const int ready_target = prep_waves + (tab_by_rest ? nwaves - prep_waves : 0);
+  const bool tab_by_rest = PACK == 1 && nw > prep_waves;
+  const int ready_target = prep_waves + (tab_by_rest ? nw - prep_waves : 0);
   float xa[10], xb[10], xc[10];
   float va[16];
   uint32_t sw_next = 0;  // sign words of the rotation unit about to be rotated
   if constexpr (ROT) {
     if (prep) {
       // the first unit's activations and sign words go out before any weight load
-      const int b = wave % nb, blk = wave / nb;
+      const int b = prank % nb, blk = prank / nb;
       load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
       sw_next = sign_bits[((g_begin >> 3) + blk) * 32 + (lane >> 1)];
     }
@@ -928,19 +936,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   uint32_t scl[F::kDepth][4];
   if (prep) {
     if (PACK == 1 && !tab_by_rest) {
-      for (int e = tid; e < 256; e += 64 * prep_waves) {
+      for (int e = prank * 64 + lane; e < 256; e += 64 * prep_waves) {
         write_b3_entry(sm.lds, uint32_t(e));
       }
     }
     if constexpr (ROT) {
-      // units wave, wave + prep_waves, ...: sign flip, rotate into this wave's
-      // scratch (inside the staging region, unused until matrix work starts),
-      // then four teams make the limbs of the block's 8 groups
-      float* L = reinterpret_cast<float*>(sm.stage + wave * kRotScratch);
+      // units prank, prank + prep_waves, ...: sign flip, rotate into this
+      // wave's scratch (inside the staging region, unused until matrix work
+      // starts, plus any LDS the launch adds for it), then four teams make the
+      // limbs of the block's 8 groups
+      float* L = reinterpret_cast<float*>(sm.stage + prank * kRotScratch);
       const int tw = lane >> 4;
-      for (int u = wave; u < units; u += prep_waves) {
+      for (int u = prank; u < units; u += prep_waves) {
         const int b = u % nb, blk = u / nb;
-        if (u != wave) {
+        if (u != prank) {
           load16_x<XDT>(xr, int64_t(b) * k + int64_t(g_begin + 8 * blk) * kGroup + 16 * lane, va);
           sw_next = sign_bits[((g_begin >> 3) + blk) * 32 + (lane >> 1)];  // this block's sign words
         }
@@ -974,15 +983,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   if (PACK == 1 && tab_by_rest && !prep) {
     // the table comes before this wave's weight loads: the loads would delay
     // it (it gates every wave's matrix work) more than it delays them
-    for (int e = tid - 64 * prep_waves; e < 256; e += 64 * (nwaves - prep_waves)) {
+    for (int e = (prank - prep_waves) * 64 + lane; e < 256; e += 64 * (nw - prep_waves)) {
       write_b3_entry(sm.lds, uint32_t(e));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the table writes come before the count
     if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+  if (comp) {
 #pragma unroll
-  for (int d = 0; d < F::kDepth; ++d)
-    issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s_lo + d, s_full, stg[d], scl[d]);
+    for (int d = 0; d < F::kDepth; ++d)
+      issue_stage<PACK, ALIGNED>(wrs, srs, src, srow_scale, s_lo + d, s_full, stg[d], scl[d]);
+  }
   // every prep wave (and table wave) has finished (each adds 1 exactly once,
   // and none waits on anything, so this ends)
   while (__hip_atomic_load(sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < ready_target)
@@ -994,7 +1005,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   for (int r = 0; r < NR; ++r) yacc[r] = 0.f;
 
   // ---- full stages, kDepth at a time so every register slot index is static
-  int s = s_lo;
+  // (waves beyond the compute waves have none)
+  int s = comp ? s_lo : s_full;
   for (; s + F::kDepth <= s_full; s += F::kDepth) {
 #pragma unroll
     for (int d = 0; d < F::kDepth; ++d)
@@ -1007,7 +1019,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
       run_stage<PACK, NR, ALIGNED>(sm, my_stage, my_stage_addr, lc, wrs, srs, src, srow_scale, s + d, s_full, nb, stg[d],
                                    scl[d], yacc);
 
-  if (has_tail) {
+  if (comp && has_tail) {
     // partial last stage: fewer groups, 2-byte granular loads straight to LDS
     const int sg = ng - s_full * kStageGroups;
     const int rb = sg * F::kGroupBytes;
@@ -1033,10 +1045,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   // ---- add the ks partial sums of each tile (through the staging buffers)
   __syncthreads();
   float* red = reinterpret_cast<float*>(my_stage);
+  if (comp) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) red[r * 64 + lane] = yacc[r];
+    for (int r = 0; r < NR; ++r) red[r * 64 + lane] = yacc[r];
+  }
   __syncthreads();
-  if (kp == 0) {
+  if (comp && kp == 0) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       float v = 0.f;
@@ -1055,17 +1069,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
 
 struct Plan {
   int rt, ks, ng;
+  bool extra_waves;  // launch 16 waves, the ones beyond rt * ks only building limbs
 };
 
-// LDS beyond the staging region that the fused rotation's scratch needs
-// (prep waves borrow the staging buffers, which are free until the matrix
-// work starts).
+// LDS beyond the staging region (ncomp compute waves' buffers) that the fused
+// rotation's scratch needs: the nw waves' prep waves borrow the staging
+// buffers, which are free until the matrix work starts.
 template <int PACK>
-constexpr int rot_extra(int nwaves, int units) {
-  const int p = nwaves < units ? nwaves : units;
-  const int need = (p < kMaxRotWaves ? p : kMaxRotWaves) * kRotScratch - nwaves * Fmt<PACK>::kStageLds;
+constexpr int rot_extra(int nw, int ncomp, int units) {
+  const int p = nw < units ? nw : units;
+  const int need = (p < kMaxRotWaves ? p : kMaxRotWaves) * kRotScratch - ncomp * Fmt<PACK>::kStageLds;
   return need > 0 ? (need + 15) / 16 * 16 : 0;
 }
+
+// Waves of a launch with ks K-part waves per tile.
+inline int launch_waves(const Plan& pl, int ks) { return pl.extra_waves ? kMaxWaves : pl.rt * ks; }
 
 template <int PACK, bool ROT>
 Plan make_plan(int b, int n, int k) {
@@ -1076,22 +1094,40 @@ Plan make_plan(int b, int n, int k) {
   // smallest tiles-per-workgroup that keeps the grid within one workgroup per CU
   int rt = 1;
   while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
-  // K-part waves per tile, then the groups per launch whose activation limbs
-  // fit in what LDS has left; fewer K-part waves leave room for more groups.
-  // At one wave per tile the room is always enough for >= 8 groups (batch <= 8).
-  int ks = kMaxWaves / rt, ng = 0;
-  for (; ks >= 1; --ks) {
-    const int extra = ROT ? rot_extra<PACK>(rt * ks, 1 << 20) : 0;
+  // Batches above 4 (two matrix-row sets) leave LDS room for few groups per
+  // launch, so few stages and few compute waves: such launches add waves
+  // that only build limbs, so the limbs take a pass or two, not eight.
+  const bool extra_waves = b > 4;
+  auto groups_for = [&](int ks) {
+    const int nw = extra_waves ? kMaxWaves : rt * ks;
+    const int extra = ROT ? rot_extra<PACK>(nw, rt * ks, 1 << 20) : 0;
     const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 134 - 46 - extra;
-    ng = room > 0 ? room / per_group : 0;
-    if (ng >= kStageGroups || ks == 1) break;
+    int ng = room > 0 ? room / per_group : 0;
+    if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
+    return ng < groups ? ng : groups;
+  };
+  int ks = 1, ng = groups_for(1);
+  if (extra_waves) {
+    // the most K-part waves that still get a stage each
+    for (int c = 2; c <= kMaxWaves / rt; ++c) {
+      const int g = groups_for(c);
+      if (g < kStageGroups || c > (g + kStageGroups - 1) / kStageGroups) break;
+      ks = c;
+      ng = g;
+    }
+  } else {
+    // K-part waves per tile, then the groups per launch whose activation limbs
+    // fit in what LDS has left; fewer K-part waves leave room for more groups.
+    // At one wave per tile the room is always enough for >= 8 groups (batch <= 8).
+    for (ks = kMaxWaves / rt; ks >= 1; --ks) {
+      ng = groups_for(ks);
+      if (ng >= kStageGroups || ks == 1) break;
+    }
   }
-  if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
-  if (ng > groups) ng = groups;
   const int nst = (ng + kStageGroups - 1) / kStageGroups;
   if (ks > nst) ks = nst;
   if (ks < 1) ks = 1;
-  return Plan{rt, ks, ng};
+  return Plan{rt, ks, ng, extra_waves};
 }
 
 template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
@@ -1112,10 +1148,11 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, c
     const int ng = groups - g0 < pl.ng ? groups - g0 : pl.ng;
     const int nst = (ng + kStageGroups - 1) / kStageGroups;
     const int ks = pl.ks < nst ? pl.ks : nst;
-    const int extra = ROT ? rot_extra<PACK>(pl.rt * ks, b * (ng / 8)) : 0;
+    const int nw = launch_waves(pl, ks);
+    const int extra = ROT ? rot_extra<PACK>(nw, pl.rt * ks, b * (ng / 8)) : 0;
     const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) +
                     pl.rt * ks * F::kStageLds + extra;
-    gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT><<<grid, 64 * pl.rt * ks, lds, s>>>(
+    gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT><<<grid, 64 * nw, lds, s>>>(
         packed, scales, xr, sign_bits, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks);
   }
 }

@@ -266,6 +266,33 @@ def test_gemv_linear_batches_above_8(packing):
         assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear", b)
 
 
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("n", [3 * synth.HIDDEN, 2 * synth.FFN], ids=["qkv_15360", "gate_up_34816"])
+def test_concatenated_linears_sampled_rows(packing, n):
+    """q/k/v and gate/up as one call each (rows concatenated): 15360 and 34816
+    rows of K = 5120, batch 1 and 8, both entry points.  The oracle computes
+    every 13th row and the last 16 (the last, partial workgroup)."""
+    k = synth.HIDDEN
+    note(f"concatenated linear {packing} {n}x{k}")
+    g = synth.rng(270, 0, n % 251, 0)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    xbits = synth.f32_to_bf16_bits(g.standard_normal((8, k)).astype(np.float32))
+    x64 = synth.bf16_bits_to_f64(xbits)
+    ref_packed, _ = PACK_REF[packing](t)
+    rows = np.unique(np.concatenate([np.arange(0, n, 13), np.arange(n - 16, n)]))
+    xr = oracle.rotate(x64, signs)
+    want = oracle.gemv(packing, ref_packed[rows], s[rows], xr, k)
+    pd, sd, sgn, xd = dev(ref_packed), scales_dev(s), signs_dev(signs), act_dev(xbits, "bf16")
+    xrd = dev(xr.astype(np.float32))
+    for b in (1, 8):
+        got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
+        assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_linear", b)
+        got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
+        assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_gemv", b)
+
+
 # ------------------------------------------------------------------ prefill product
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
