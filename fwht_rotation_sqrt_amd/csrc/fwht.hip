@@ -119,15 +119,7 @@ __global__ __launch_bounds__(64 * kWaves) void fwht1024_kernel(const void* x, vo
 
   butterfly16(v);  // index bits 4..7
 
-  // index bits 8, 9 are lane bits 4, 5
-#pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float o = __shfl_xor(v[j], m, 64);
-      v[j] = (lane & m) ? (o - v[j]) : (v[j] + o);
-    }
-  }
+  butterfly_lane_bits_4_5(v, lane);  // index bits 8, 9 are lane bits 4, 5
 
   __syncthreads();
 #pragma unroll

@@ -291,13 +291,7 @@ __device__ __forceinline__ void rotate_block(float (&v)[16], float* L, int lane)
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = L[bidx + 17 * j];
   butterfly16(v);  // index bits 4..7
-#pragma unroll
-  for (int m = 16; m <= 32; m <<= 1)  // index bits 8, 9 = lane bits 4, 5
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float o = __shfl_xor(v[j], m, 64);
-      v[j] = (lane & m) ? (o - v[j]) : (v[j] + o);
-    }
+  butterfly_lane_bits_4_5(v, lane);  // index bits 8, 9 = lane bits 4, 5
   wave_fence();
 #pragma unroll
   for (int j = 0; j < 16; ++j) L[bidx + 17 * j] = v[j] * 0.03125f;
@@ -414,10 +408,12 @@ __device__ __forceinline__ void limbs_for_group(const Smem& sm, int b, int g, in
     }
   }
   if constexpr (PACK == 0) sum = row16_sum(sum);  // only the 2-bit path needs it
-  if (l16 == 0) {
-    sm.f[b * sm.ng + g] = make_float2(ldexpf(1.f, -sig), sum);
-    sm.e0[b * e0_stride(sm.ng) + g] = uint8_t(127 - sig);
-  }
+  // every lane of the team holds the same sig and sum (the butterfly
+  // reductions leave the result in all 16 lanes), so all store: the same
+  // bytes to the same address, and no branch splits the caller's code, which
+  // lets the limbs of two groups interleave
+  sm.f[b * sm.ng + g] = make_float2(ldexpf(1.f, -sig), sum);
+  sm.e0[b * e0_stride(sm.ng) + g] = uint8_t(127 - sig);
 }
 
 // ---------------------------------------------------------------- matrix work

@@ -27,4 +27,27 @@ void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, con
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);
 
+// Walsh-Hadamard butterflies across lane bits 4 and 5 of a wave (partner
+// lane l ^ 16, then l ^ 32), for 16 values per lane: the lane whose bit is 0
+// keeps own + partner, the other partner - own.  The permlane swaps are
+// VALU operations (no LDS round trip).  With both operands the same value, a
+// swap returns (own, partner) in lanes whose bit is 0 and (partner, own) in
+// the others, so one fused multiply-add by +-1 (exact: a single rounding of
+// the sum or difference) finishes each butterfly.
+__device__ __forceinline__ void butterfly_lane_bits_4_5(float (&v)[16], int lane) {
+  const float s16 = (lane & 16) ? -1.f : 1.f, s32 = (lane & 32) ? -1.f : 1.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t u = __float_as_uint(v[j]);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v[j] = fmaf(s16, __uint_as_float(p[1]), __uint_as_float(p[0]));
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t u = __float_as_uint(v[j]);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v[j] = fmaf(s32, __uint_as_float(p[1]), __uint_as_float(p[0]));
+  }
+}
+
 }  // namespace tb
