@@ -230,7 +230,7 @@ __device__ __forceinline__ void load_x(const void* __restrict__ xr, int k, int b
 // scratch (element i at i + i/16, padded against bank conflicts) for the
 // limb teams.
 constexpr int kRotScratch = 1088 * 4;  // bytes of one wave's scratch
-constexpr int kMaxRotWaves = 8;
+constexpr int kMaxRotWaves = 16;  // rotation waves per workgroup, when LDS holds their scratch
 
 template <int DT>
 __device__ __forceinline__ void load16_x(const void* base, int64_t off, float (&v)[16]) {
@@ -817,7 +817,7 @@ template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, const void* __restrict__ xr,
     const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int nb, int n, int k, int g_begin, int ng,
-    int accumulate, int rt, int ks) {
+    int accumulate, int rt, int ks, int rot_waves) {
   using F = Fmt<PACK>;
   extern __shared__ __align__(16) uint8_t smem[];
   // the wave index through readfirstlane: per-wave quantities below become
@@ -879,7 +879,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   const int prank = comp ? wave + (nw - ncomp) : wave - ncomp;
   // rotation units: (batch, block) pairs, one wave each at a time
   const int nblk = ng / 8, units = nb * nblk;
-  const int prep_waves = ROT ? min(min(nw, units), kMaxRotWaves)
+  const int prep_waves = ROT ? min(min(nw, units), rot_waves)
                              : max(nw - ncomp, min(nw, (pairs + 11) / 12));  // ~3 (batch, group) pairs per team
   const bool prep = prank < prep_waves;
   const int team = prank * (64 / kTeam) + (lane >> 4), l16 = lane & (kTeam - 1), nteams = prep_waves * (64 / kTeam);
@@ -1066,15 +1066,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
 struct Plan {
   int rt, ks, ng;
   bool extra_waves;  // launch 16 waves, the ones beyond rt * ks only building limbs
+  int rot_waves;     // fused rotation: most waves that rotate at once (their scratch is in LDS)
 };
 
 // LDS beyond the staging region (ncomp compute waves' buffers) that the fused
 // rotation's scratch needs: the nw waves' prep waves borrow the staging
 // buffers, which are free until the matrix work starts.
 template <int PACK>
-constexpr int rot_extra(int nw, int ncomp, int units) {
+constexpr int rot_extra(int nw, int ncomp, int units, int rot_waves) {
   const int p = nw < units ? nw : units;
-  const int need = (p < kMaxRotWaves ? p : kMaxRotWaves) * kRotScratch - ncomp * Fmt<PACK>::kStageLds;
+  const int need = (p < rot_waves ? p : rot_waves) * kRotScratch - ncomp * Fmt<PACK>::kStageLds;
   return need > 0 ? (need + 15) / 16 * 16 : 0;
 }
 
@@ -1082,7 +1083,7 @@ constexpr int rot_extra(int nw, int ncomp, int units) {
 inline int launch_waves(const Plan& pl, int ks) { return pl.extra_waves ? kMaxWaves : pl.rt * ks; }
 
 template <int PACK, bool ROT>
-Plan make_plan(int b, int n, int k) {
+Plan make_plan(int b, int n, int k, int rot_waves, bool extra_waves) {
   using F = Fmt<PACK>;
   const int tiles = (n + 15) / 16;
   const int groups = k / kGroup;
@@ -1090,13 +1091,9 @@ Plan make_plan(int b, int n, int k) {
   // smallest tiles-per-workgroup that keeps the grid within one workgroup per CU
   int rt = 1;
   while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
-  // Batches above 4 (two matrix-row sets) leave LDS room for few groups per
-  // launch, so few stages and few compute waves: such launches add waves
-  // that only build limbs, so the limbs take a pass or two, not eight.
-  const bool extra_waves = b > 4;
   auto groups_for = [&](int ks) {
     const int nw = extra_waves ? kMaxWaves : rt * ks;
-    const int extra = ROT ? rot_extra<PACK>(nw, rt * ks, 1 << 20) : 0;
+    const int extra = ROT ? rot_extra<PACK>(nw, rt * ks, 1 << 20, rot_waves) : 0;
     const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 134 - 46 - extra;
     int ng = room > 0 ? room / per_group : 0;
     if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
@@ -1104,10 +1101,12 @@ Plan make_plan(int b, int n, int k) {
   };
   int ks = 1, ng = groups_for(1);
   if (extra_waves) {
-    // the most K-part waves that still get a stage each
+    // fewest launches first (the most groups per launch), then the most
+    // K-part waves that still get a stage each
     for (int c = 2; c <= kMaxWaves / rt; ++c) {
       const int g = groups_for(c);
       if (g < kStageGroups || c > (g + kStageGroups - 1) / kStageGroups) break;
+      if ((groups + g - 1) / g > (groups + ng - 1) / ng) break;
       ks = c;
       ng = g;
     }
@@ -1123,7 +1122,7 @@ Plan make_plan(int b, int n, int k) {
   const int nst = (ng + kStageGroups - 1) / kStageGroups;
   if (ks > nst) ks = nst;
   if (ks < 1) ks = 1;
-  return Plan{rt, ks, ng, extra_waves};
+  return Plan{rt, ks, ng, extra_waves, rot_waves};
 }
 
 template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
@@ -1131,7 +1130,24 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, c
                 int b, int n, int k, hipStream_t s) {
   using F = Fmt<PACK>;
   const int groups = k / kGroup;
-  const Plan pl = make_plan<PACK, ROT>(b, n, k);
+  // Batches of 2 and more leave LDS room for fewer groups per launch, so a
+  // launch may get few stages and few compute waves.  Such launches run 16
+  // waves, the ones beyond the compute waves only building limbs (a pass or
+  // two instead of up to eight), when that saves a launch or the plain plan
+  // has at most 8 waves.  Then eight rotation waves, unless the launch has
+  // 15 or more waves and sixteen fit without more launches or fewer K-part
+  // waves (with fewer waves, rotating on all of them delays every weight
+  // load: 2-bit 5120 x 5120 at batch 4 lost 1.4 us).
+  auto launches = [&](const Plan& p) { return p.ng >= 1 ? (groups + p.ng - 1) / p.ng : 1 << 30; };
+  Plan pl = make_plan<PACK, ROT>(b, n, k, 8, false);
+  if (b > 1) {
+    const Plan px = make_plan<PACK, ROT>(b, n, k, 8, true);
+    if (launches(px) < launches(pl) || (launches(px) == launches(pl) && pl.rt * pl.ks <= 8)) pl = px;
+  }
+  if (ROT && (pl.extra_waves || pl.rt * pl.ks >= 15)) {
+    const Plan p16 = make_plan<PACK, ROT>(b, n, k, kMaxRotWaves, pl.extra_waves);
+    if (launches(p16) <= launches(pl) && p16.ks >= pl.ks) pl = p16;
+  }
   if (pl.ng < 1) return;  // unreachable for batch <= 8 (see make_plan); never loop without progress
   static std::once_flag once;
   std::call_once(once, [] {
@@ -1145,11 +1161,11 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, c
     const int nst = (ng + kStageGroups - 1) / kStageGroups;
     const int ks = pl.ks < nst ? pl.ks : nst;
     const int nw = launch_waves(pl, ks);
-    const int extra = ROT ? rot_extra<PACK>(nw, pl.rt * ks, b * (ng / 8)) : 0;
+    const int extra = ROT ? rot_extra<PACK>(nw, pl.rt * ks, b * (ng / 8), pl.rot_waves) : 0;
     const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) +
                     pl.rt * ks * F::kStageLds + extra;
     gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT><<<grid, 64 * nw, lds, s>>>(
-        packed, scales, xr, sign_bits, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks);
+        packed, scales, xr, sign_bits, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks, pl.rot_waves);
   }
 }
 
