@@ -270,8 +270,9 @@ def test_gemv_linear_batches_above_8(packing):
 @pytest.mark.parametrize("n", [3 * synth.HIDDEN, 2 * synth.FFN], ids=["qkv_15360", "gate_up_34816"])
 def test_concatenated_linears_sampled_rows(packing, n):
     """q/k/v and gate/up as one call each (rows concatenated): 15360 and 34816
-    rows of K = 5120, batch 1 and 8, both entry points.  The oracle computes
-    every 13th row and the last 16 (the last, partial workgroup)."""
+    rows of K = 5120, batch 1, 3 and 8, both entry points (34816 rows put 9
+    row tiles in a workgroup).  The oracle computes every 13th row and the
+    last 16 (the last, partial workgroup)."""
     k = synth.HIDDEN
     note(f"concatenated linear {packing} {n}x{k}")
     g = synth.rng(270, 0, n % 251, 0)
@@ -286,7 +287,7 @@ def test_concatenated_linears_sampled_rows(packing, n):
     want = oracle.gemv(packing, ref_packed[rows], s[rows], xr, k)
     pd, sd, sgn, xd = dev(ref_packed), scales_dev(s), signs_dev(signs), act_dev(xbits, "bf16")
     xrd = dev(xr.astype(np.float32))
-    for b in (1, 8):
+    for b in (1, 3, 8):
         got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
         assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_linear", b)
         got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
