@@ -370,6 +370,17 @@ def suite_read_calibration(reps=10):
             "copy_us": t_copy * 1e6, "copy_gbs": (2 << 30) / t_copy / 1e9}
 
 
+def shader_clock():
+    """The current sclk line of rocm-smi, or a note that it was not available."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        lines = [l.strip() for l in out.splitlines() if "sclk" in l.lower()]
+        return lines[0] if lines else "not reported"
+    except Exception as e:  # noqa: BLE001
+        return f"not available ({type(e).__name__})"
+
+
 def run_suite(path, argv):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(SUITE_SEED)
@@ -384,8 +395,17 @@ def run_suite(path, argv):
                 rows.append((lin, packing, b, r))
                 print(f"{lin.name} {lin.n}x{lin.k} {packing} b{b}: fused {r['fused']:.2f} us, "
                       f"rotate {r['rotate']:.2f} + gemv {r['gemv']:.2f} us", flush=True)
+    # batches above 8 (chunks of 8 rows over the weights) on the FFN linear
+    big = []
+    gate = synth.BLOCK_LINEARS[4]
+    for packing in ("2bit", "base3"):
+        for b in (2, 4, 16, 32):
+            r = suite_linear(packing, gate.n, gate.k, b, gen, steps=20)
+            big.append((packing, b, r))
+            print(f"gate {packing} b{b}: fused {r['fused']:.2f} us, gemv {r['gemv']:.2f} us", flush=True)
     tok = suite_token(gen)
     print(f"token: fused {tok['fused'] * 1e3:.3f} ms, separate {tok['separate'] * 1e3:.3f} ms", flush=True)
+    sclk = shader_clock()
 
     pk = HBM_PEAK_GBS
     lines.append("# Block linears and the 64-layer decode token stream (MI355X, one GPU)")
@@ -410,6 +430,15 @@ def run_suite(path, argv):
         lines.append(f"| {lin.name} | {lin.n}x{lin.k} | {packing} | {b} | {r['bytes'] / 1e6:.2f} | {r['fused']:.2f} | "
                      f"{gbs:.0f} | {100 * gbs / pk:.1f} | {r['rotate']:.2f} | {r['gemv']:.2f} |")
     lines.append("")
+    lines.append("## Other batch sizes on gate (17408x5120)")
+    lines.append("")
+    lines.append("Batches above 8 run as chunks of 8 rows, each streaming the weights again.")
+    lines.append("")
+    lines.append("| packing | batch | tb_linear us | tb_gemv us | weight GB/s (tb_linear) |")
+    lines.append("|---|---|---|---|---|")
+    for packing, b, r in big:
+        lines.append(f"| {packing} | {b} | {r['fused']:.2f} | {r['gemv']:.2f} | {r['bytes'] / (r['fused'] * 1e-6) / 1e9:.0f} |")
+    lines.append("")
     lines.append("## Decode token stream: 64 layers, base-3, batch 1 (q/k/v and gate/up concatenated)")
     lines.append("")
     t_f, t_s, t_r, t_g = tok["fused"], tok["separate"], tok["rotate_only"], tok["gemv_only"]
@@ -428,6 +457,8 @@ def run_suite(path, argv):
         n, k, t = tok["call_" + nm]
         byts = n * (tb.tb_packed_row_bytes("base3", k) + 2 * (k // 128))
         lines.append(f"| {nm} | {n}x{k} | {t * 1e6:.2f} | {byts / t / 1e9:.0f} |")
+    lines.append("")
+    lines.append(f"Shader clock reported by rocm-smi after the run: {sclk}.")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"suite": path, "token_ms_fused": round(t_f * 1e3, 4),
