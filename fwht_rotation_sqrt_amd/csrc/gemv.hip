@@ -71,9 +71,12 @@ struct Fmt {
   static constexpr int kStageChunks = 16 * kChunksPerRow;       // 256 or 208
   static constexpr int kLoads = (kStageChunks + 63) / 64;       // 4
   static constexpr int kStageLds = 16 * kRowLds + 32;           // + pad for operand over-reads
-  // base-3 table: entry e at byte 256 e, copy c (lane & 31) at + 4c, so one
-  // byte permute forms the address (e << 8) | 4c from the staged bytes
-  static constexpr int kTable = PACK == 1 ? 256 * 256 : 0;
+  // base-3 table: entry e at byte 256 e (PACK 1, 64 KB) or 128 e (PACK 2,
+  // 32 KB, for launches that need the LDS), copy c (lane & 31) at + 4c.  One
+  // byte permute forms (e << 8) | 4c from the staged bytes, or (e << 8) | 8c
+  // and a shift halves it.
+  static constexpr int kTable = PACK == 1 ? 256 * 256 : PACK == 2 ? 128 * 256 : 0;
+  static constexpr int kEntry = PACK == 2 ? 128 : 256;  // base-3 table entry stride
 };
 
 // Activation limb rows in LDS: 128 K-slot bytes padded to 36 dwords so the
@@ -131,7 +134,7 @@ __host__ __device__ constexpr int b3_tau_of_slot(int s) {
 // factors, then the waves' staging buffers.
 // A operand slot s of lane group q' reads K-slot 16q'+s (s < 16) or 64+16q'+s-16.
 struct Smem {
-  uint8_t* lds;     // LDS address 0: the base-3 table, 256 entries x 256 bytes
+  uint8_t* lds;     // LDS address 0: the base-3 table, 256 entries x 256 (or 128) bytes
   uint8_t* a;       // [B][ng][mfmas][3][144] activation limbs in K-slot order
   int a_bstride;    // bytes between batches in a
   float2* f;        // [B][ng] = {2^-sig, sum of reconstructed activations}
@@ -168,11 +171,12 @@ __device__ __forceinline__ uint32_t base3_t_nibbles(uint32_t e) {
   return v;
 }
 
-// Table entry e at LDS byte 256 e: kCopies copies of its trit nibbles, one
+// Table entry e at LDS byte kEntry e: kCopies copies of its trit nibbles, one
 // per lane of a half-wave, so the lanes' lookups fall in distinct banks.
+template <int PACK>
 __device__ __forceinline__ void write_b3_entry(uint8_t* lds, uint32_t e) {
   const uint32_t v = base3_t_nibbles(e);
-  uint4* dst = reinterpret_cast<uint4*>(lds + 256 * e);
+  uint4* dst = reinterpret_cast<uint4*>(lds + Fmt<PACK>::kEntry * e);
 #pragma unroll
   for (int i = 0; i < kCopies / 4; ++i) dst[i] = make_uint4(v, v, v, v);
 
@@ -583,14 +587,16 @@ __device__ __forceinline__ void b3r_read_bytes(const LaneCtx& lc, uint32_t bo, u
 // table (its five trits as nibbles 0..4 of a dword), shifted and ORed into
 // 32 dense nibbles: bytes 6q .. 6q + 5 in slots 0..29 and two of the ten
 // trits of bytes 24, 25 in slots 30, 31.
-template <int P>
+template <int PACK, int P>
 __device__ __forceinline__ v8i b3r_make_bop(const LaneCtx& lc, const uint32_t (&raw)[4]) {
   const uint32_t sh = lc.b3_sh[P];
   const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);
   const uint32_t w1 = raw[1] >> (8 * sh);
   auto look = [&](uint32_t w, int byte) -> uint32_t {
-    // address bytes: [0] = lane copy offset, [1] = the code byte, [2..3] = 0
-    return lds_read<uint32_t>(__builtin_amdgcn_perm(lc.tab, w, 0x0C0C0004u | (uint32_t(byte) << 8)));
+    // permuted bytes: [0] = lane copy offset (times 2 for PACK 2), [1] = the
+    // code byte, [2..3] = 0; PACK 2 halves it to 128 x byte + 4 x copy
+    const uint32_t a = __builtin_amdgcn_perm(lc.tab, w, 0x0C0C0004u | (uint32_t(byte) << 8));
+    return lds_read<uint32_t>(PACK == 2 ? a >> 1 : a);
   };
   const uint32_t e0 = look(w0, 0), e1 = look(w0, 1), e2 = look(w0, 2), e3 = look(w0, 3);
   const uint32_t e4 = look(w1, 0), e5 = look(w1, 1);
@@ -628,11 +634,11 @@ struct B3Pipe {
 // A row (batch, limb) by 2^-sig 16^-limb through its E8M0 scale (byte P of
 // ex[r][0]), so a result is just s (d0 + d1 + d2); the group's fp16 scale s
 // is half P of sq0.
-template <int NR, int P>
+template <int PACK, int NR, int P>
 __device__ __forceinline__ void b3r_group_step(const LaneCtx& lc, uint32_t bo, int gc, uint32_t sq0, B3Pipe<NR>& st,
                                                float (&yacc)[NR]) {
   __builtin_amdgcn_sched_barrier(0);
-  const v8i bop = b3r_make_bop<P>(lc, st.raw[P]);
+  const v8i bop = b3r_make_bop<PACK, P>(lc, st.raw[P]);
   v8i aops[NR];
   b3r_load_aop<NR>(lc, gc, aops);
   // the next group's bytes (past the stage's last group: the row padding, ignored)
@@ -654,7 +660,7 @@ __device__ __forceinline__ void b3r_group_step(const LaneCtx& lc, uint32_t bo, i
 
 // All groups of one staged block of sg (1..8) base-3 groups starting at group
 // gc0 of the launch, two per iteration of a rolled loop.
-template <int NR>
+template <int PACK, int NR>
 __device__ __forceinline__ void b3r_stage_compute(uint32_t stage, const LaneCtx& lc, int sg, int gc0,
                                                   const uint32_t (&sreg)[4], float (&yacc)[NR]) {
   B3Pipe<NR> st;
@@ -674,8 +680,8 @@ __device__ __forceinline__ void b3r_stage_compute(uint32_t stage, const LaneCtx&
   int g = 0;
 #pragma unroll 1
   for (; g + 1 < sg; g += 2) {
-    b3r_group_step<NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
-    b3r_group_step<NR, 1>(lc, bo, gc0 + g + 1, sq[0], st, yacc);
+    b3r_group_step<PACK, NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
+    b3r_group_step<PACK, NR, 1>(lc, bo, gc0 + g + 1, sq[0], st, yacc);
     bo += 2 * kB3GroupBytes;
     sq[0] = sq[1];
     sq[1] = sq[2];
@@ -686,7 +692,7 @@ __device__ __forceinline__ void b3r_stage_compute(uint32_t stage, const LaneCtx&
       st.ex[r][1] >>= 16;
     }
   }
-  if (g < sg) b3r_group_step<NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
+  if (g < sg) b3r_group_step<PACK, NR, 0>(lc, bo, gc0 + g, sq[0], st, yacc);
 #pragma unroll
   for (int r = 0; r < NR; ++r) yacc[r] = fmaf(st.sprev, st.prev[r][0] + st.prev[r][1] + st.prev[r][2], yacc[r]);
 }
@@ -696,8 +702,8 @@ __device__ __forceinline__ void b3r_stage_compute(uint32_t stage, const LaneCtx&
 template <int PACK, int NR>
 __device__ __forceinline__ void stage_compute(const Smem& sm, uint32_t stage, const LaneCtx& lc, int sg,
                                               int gc0, const uint32_t (&sreg)[4], float (&yacc)[NR]) {
-  if constexpr (PACK == 1) {
-    b3r_stage_compute<NR>(stage, lc, sg, gc0, sreg, yacc);
+  if constexpr (PACK != 0) {
+    b3r_stage_compute<PACK, NR>(stage, lc, sg, gc0, sreg, yacc);
     return;
   }
   StageBase sb;
@@ -860,7 +866,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     lc.e_lane[r] = uint32_t(F::kTable + a_bytes + f_bytes(nb, ng) + b * e0_stride(ng));
     lc.f_lane[r] = min(4 * r + q, nb - 1) * ng;
   }
-  lc.tab = uint32_t(4 * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
+  lc.tab = uint32_t((PACK == 2 ? 8 : 4) * (lane & (kCopies - 1)));  // < 256: fits the permute's byte 0
 
   // ---- roles.  Waves 0 .. rt*ks - 1 own row tiles and stages (compute
   // waves); a launch may add waves beyond them that only build limbs (more
@@ -886,7 +892,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   // The base-3 decode table is written by the waves that build no limbs
   // (they would otherwise sit idle until the limbs are ready), or by the prep
   // waves when every wave is one.  Each table wave adds 1 to the ready count.
-  const bool tab_by_rest = PACK == 1 && nw > prep_waves;
+  const bool tab_by_rest = PACK != 0 && nw > prep_waves;
   const int ready_target = prep_waves + (tab_by_rest ? nw - prep_waves : 0);
   float xa[10], xb[10], xc[10];
   float va[16];
@@ -931,9 +937,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
   uint4 stg[F::kDepth][F::kLoads];
   uint32_t scl[F::kDepth][4];
   if (prep) {
-    if (PACK == 1 && !tab_by_rest) {
+    if (PACK != 0 && !tab_by_rest) {
       for (int e = prank * 64 + lane; e < 256; e += 64 * prep_waves) {
-        write_b3_entry(sm.lds, uint32_t(e));
+        write_b3_entry<PACK>(sm.lds, uint32_t(e));
       }
     }
     if constexpr (ROT) {
@@ -976,11 +982,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  if (PACK == 1 && tab_by_rest && !prep) {
+  if (PACK != 0 && tab_by_rest && !prep) {
     // the table comes before this wave's weight loads: the loads would delay
     // it (it gates every wave's matrix work) more than it delays them
     for (int e = (prank - prep_waves) * 64 + lane; e < 256; e += 64 * (nw - prep_waves)) {
-      write_b3_entry(sm.lds, uint32_t(e));
+      write_b3_entry<PACK>(sm.lds, uint32_t(e));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the table writes come before the count
     if (lane == 0) __hip_atomic_fetch_add(sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1067,88 +1073,107 @@ struct Plan {
   int rt, ks, ng;
   bool extra_waves;  // launch 16 waves, the ones beyond rt * ks only building limbs
   int rot_waves;     // fused rotation: most waves that rotate at once (their scratch is in LDS)
+  int kind;          // kernel packing kind: 0 2-bit, 1 base-3, 2 base-3 with the 32 KB table
 };
 
 // LDS beyond the staging region (ncomp compute waves' buffers) that the fused
 // rotation's scratch needs: the nw waves' prep waves borrow the staging
 // buffers, which are free until the matrix work starts.
-template <int PACK>
-constexpr int rot_extra(int nw, int ncomp, int units, int rot_waves) {
+inline int rot_extra(int stage_lds, int nw, int ncomp, int units, int rot_waves) {
   const int p = nw < units ? nw : units;
-  const int need = (p < rot_waves ? p : rot_waves) * kRotScratch - ncomp * Fmt<PACK>::kStageLds;
+  const int need = (p < rot_waves ? p : rot_waves) * kRotScratch - ncomp * stage_lds;
   return need > 0 ? (need + 15) / 16 * 16 : 0;
 }
 
-// Waves of a launch with ks K-part waves per tile.
-inline int launch_waves(const Plan& pl, int ks) { return pl.extra_waves ? kMaxWaves : pl.rt * ks; }
+template <int PACK>
+struct KindInfo {
+  static constexpr int kTable = Fmt<PACK>::kTable, kStageLds = Fmt<PACK>::kStageLds;
+};
 
-template <int PACK, bool ROT>
-Plan make_plan(int b, int n, int k, int rot_waves, bool extra_waves) {
-  using F = Fmt<PACK>;
-  const int tiles = (n + 15) / 16;
-  const int groups = k / kGroup;
-  const int per_group = F::kMfmas * b * kAGroup + b * 9;  // + b * 127 bytes of batch padding, b * 7 of e0 rows
-  // smallest tiles-per-workgroup that keeps the grid within one workgroup per CU
-  int rt = 1;
-  while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
-  auto groups_for = [&](int ks) {
-    const int nw = extra_waves ? kMaxWaves : rt * ks;
-    const int extra = ROT ? rot_extra<PACK>(nw, rt * ks, 1 << 20, rot_waves) : 0;
-    const int room = kLdsBytes - F::kTable - rt * ks * F::kStageLds - b * 134 - 46 - extra;
-    int ng = room > 0 ? room / per_group : 0;
-    if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
-    return ng < groups ? ng : groups;
-  };
-  int ks = 1, ng = groups_for(1);
-  if (extra_waves) {
-    // fewest launches first (the most groups per launch), then the most
-    // K-part waves that still get a stage each
-    for (int c = 2; c <= kMaxWaves / rt; ++c) {
-      const int g = groups_for(c);
-      if (g < kStageGroups || c > (g + kStageGroups - 1) / kStageGroups) break;
-      if ((groups + g - 1) / g > (groups + ng - 1) / ng) break;
-      ks = c;
-      ng = g;
-    }
-  } else {
-    // K-part waves per tile, then the groups per launch whose activation limbs
-    // fit in what LDS has left; fewer K-part waves leave room for more groups.
-    // At one wave per tile the room is always enough for >= 8 groups (batch <= 8).
-    for (ks = kMaxWaves / rt; ks >= 1; --ks) {
-      ng = groups_for(ks);
-      if (ng >= kStageGroups || ks == 1) break;
+// Groups per launch whose limbs fit in the LDS the other regions leave, for
+// ks K-part waves per tile (a multiple of 8 when at least 8).
+inline int plan_groups(int table, int stage_lds, bool rot, int b, int groups, int rt, int ks, bool extra,
+                       int rot_waves) {
+  const int nw = extra ? kMaxWaves : rt * ks;
+  const int ex = rot ? rot_extra(stage_lds, nw, rt * ks, 1 << 20, rot_waves) : 0;
+  const int room = kLdsBytes - table - rt * ks * stage_lds - b * 134 - 46 - ex;
+  const int per_group = kAGroup * b + b * 9;  // + b * 127 bytes of batch padding, b * 7 of e0 rows
+  int ng = room > 0 ? room / per_group : 0;
+  if (ng >= kStageGroups) ng = ng / kStageGroups * kStageGroups;
+  return ng < groups ? ng : groups;
+}
+
+// Estimated time of a plan, in rough microseconds, from what measurements
+// show dominates: a fixed cost per launch (launch, activation fetch, table),
+// the longest wave's stages (about 2 us each; 8 % more with the 32 KB table,
+// whose lookups take a shift), the limb passes (about 0.6 us each) or, when
+// the rotation is fused, the rotation-and-limb passes (about 1.3 us each; a
+// launch whose every wave rotates issues no weight load meanwhile: +1.5 us).
+inline double plan_cost(bool rot, int b, int groups, int rt, int ks, int ng, bool extra, int rot_waves,
+                        bool compact) {
+  double c = 0.0;
+  for (int g0 = 0; g0 < groups; g0 += ng) {
+    const int ngi = groups - g0 < ng ? groups - g0 : ng;
+    const int nst = (ngi + kStageGroups - 1) / kStageGroups;
+    const int ksi = ks < nst ? ks : nst;
+    const int ncomp = rt * ksi, nw = extra ? kMaxWaves : ncomp;
+    const int crit = (nst + ksi - 1) / ksi;
+    c += 4.0 + crit * 2.0 * (compact ? 1.08 : 1.0);
+    if (rot) {
+      const int units = b * (ngi / kStageGroups);
+      int rw = nw < units ? nw : units;
+      rw = rw < rot_waves ? rw : rot_waves;
+      c += ((units + rw - 1) / rw) * 1.3;
+      if (rw >= nw && nw < 15) c += 1.5;
+    } else {
+      const int pairs = b * ngi;
+      const int by_need = (pairs + 11) / 12;
+      int pw = nw < by_need ? nw : by_need;
+      if (nw - ncomp > pw) pw = nw - ncomp;
+      c += ((pairs + 4 * pw - 1) / (4 * pw)) * 0.6;
     }
   }
-  const int nst = (ng + kStageGroups - 1) / kStageGroups;
-  if (ks > nst) ks = nst;
-  if (ks < 1) ks = 1;
-  return Plan{rt, ks, ng, extra_waves, rot_waves};
+  return c;
+}
+
+// The cheapest base-3 plan over: the table size (64 KB, or 32 KB when the
+// room buys fewer launches or more K-part waves), limb-only waves or not
+// (batches of 2 and more), 8 or 16 rotation waves, and the K-part waves per
+// tile.  rt, the tiles per workgroup, is the smallest that keeps the grid
+// within one workgroup per CU.
+template <bool ROT>
+Plan make_plan(int packing, int b, int n, int k) {
+  const int tiles = (n + 15) / 16;
+  const int groups = k / kGroup;
+  int rt = 1;
+  while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
+  Plan best{rt, 1, 0, false, 8, packing == 0 ? 0 : 1};
+  double best_cost = 1e30;
+  for (int kind = packing == 0 ? 0 : 1; kind <= (packing == 0 ? 0 : 2); ++kind) {
+    const int table = kind == 0 ? KindInfo<0>::kTable : kind == 1 ? KindInfo<1>::kTable : KindInfo<2>::kTable;
+    const int stage_lds = kind == 0 ? KindInfo<0>::kStageLds : KindInfo<1>::kStageLds;
+    for (int extra = 0; extra <= (b > 1 ? 1 : 0); ++extra)
+      for (int rw = 8; rw <= (ROT ? kMaxRotWaves : 8); rw += 8)
+        for (int ks = kMaxWaves / rt; ks >= 1; --ks) {
+          const int ng = plan_groups(table, stage_lds, ROT, b, groups, rt, ks, extra != 0, rw);
+          if (ng < 1 || (ROT && ng % kStageGroups != 0)) continue;
+          if (ng < kStageGroups && ng < groups && ks > 1) continue;
+          if (ks > (ng + kStageGroups - 1) / kStageGroups) continue;
+          const double c = plan_cost(ROT, b, groups, rt, ks, ng, extra != 0, rw, kind == 2);
+          if (c < best_cost - 1e-9) {
+            best_cost = c;
+            best = Plan{rt, ks, ng, extra != 0, rw, kind};
+          }
+        }
+  }
+  return best;
 }
 
 template <int PACK, int NR, int XDT, bool ALIGNED, bool ROT>
-void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, const uint32_t* sign_bits, float* y,
-                int b, int n, int k, hipStream_t s) {
+void run_plan(const Plan& pl, const uint8_t* packed, const uint16_t* scales, const void* xr,
+              const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s) {
   using F = Fmt<PACK>;
   const int groups = k / kGroup;
-  // Batches of 2 and more leave LDS room for fewer groups per launch, so a
-  // launch may get few stages and few compute waves.  Such launches run 16
-  // waves, the ones beyond the compute waves only building limbs (a pass or
-  // two instead of up to eight), when that saves a launch or the plain plan
-  // has at most 8 waves.  Then eight rotation waves, unless the launch has
-  // 15 or more waves and sixteen fit without more launches or fewer K-part
-  // waves (with fewer waves, rotating on all of them delays every weight
-  // load: 2-bit 5120 x 5120 at batch 4 lost 1.4 us).
-  auto launches = [&](const Plan& p) { return p.ng >= 1 ? (groups + p.ng - 1) / p.ng : 1 << 30; };
-  Plan pl = make_plan<PACK, ROT>(b, n, k, 8, false);
-  if (b > 1) {
-    const Plan px = make_plan<PACK, ROT>(b, n, k, 8, true);
-    if (launches(px) < launches(pl) || (launches(px) == launches(pl) && pl.rt * pl.ks <= 8)) pl = px;
-  }
-  if (ROT && (pl.extra_waves || pl.rt * pl.ks >= 15)) {
-    const Plan p16 = make_plan<PACK, ROT>(b, n, k, kMaxRotWaves, pl.extra_waves);
-    if (launches(p16) <= launches(pl) && p16.ks >= pl.ks) pl = p16;
-  }
-  if (pl.ng < 1) return;  // unreachable for batch <= 8 (see make_plan); never loop without progress
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT>),
@@ -1160,12 +1185,72 @@ void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, c
     const int ng = groups - g0 < pl.ng ? groups - g0 : pl.ng;
     const int nst = (ng + kStageGroups - 1) / kStageGroups;
     const int ks = pl.ks < nst ? pl.ks : nst;
-    const int nw = launch_waves(pl, ks);
-    const int extra = ROT ? rot_extra<PACK>(nw, pl.rt * ks, b * (ng / 8), pl.rot_waves) : 0;
+    const int nw = pl.extra_waves ? kMaxWaves : pl.rt * ks;
+    const int extra = ROT ? rot_extra(F::kStageLds, nw, pl.rt * ks, b * (ng / 8), pl.rot_waves) : 0;
     const int lds = F::kTable + b * a_batch_stride(ng, F::kMfmas) + f_region_bytes(b, ng) +
                     pl.rt * ks * F::kStageLds + extra;
     gemv_mfma_kernel<PACK, NR, XDT, ALIGNED, ROT><<<grid, 64 * nw, lds, s>>>(
         packed, scales, xr, sign_bits, y, b, n, k, g0, ng, g0 > 0 ? 1 : 0, pl.rt, ks, pl.rot_waves);
+  }
+}
+
+// The 2-bit plan (its loop is faster, so the cost weights above, set on
+// base-3, misjudge it): the most K-part waves whose limbs still leave room for
+// a stage each; 16 waves with limb-only ones when that saves a launch or the
+// plain plan has at most 8 waves; 16 rotation waves when the launch has 15 or
+// more waves (or limb-only ones) and they fit without more launches.
+template <bool ROT>
+Plan make_plan_2bit(int b, int n, int k) {
+  const int tiles = (n + 15) / 16;
+  const int groups = k / kGroup;
+  const int table = KindInfo<0>::kTable, stage_lds = KindInfo<0>::kStageLds;
+  int rt = 1;
+  while (rt < kMaxWaves && (tiles + rt - 1) / rt > 256) ++rt;
+  auto plan = [&](bool extra, int rw) {
+    int ks = 1, ng = plan_groups(table, stage_lds, ROT, b, groups, rt, 1, extra, rw);
+    if (extra) {
+      // fewest launches first, then the most K-part waves that still get a stage each
+      for (int c = 2; c <= kMaxWaves / rt; ++c) {
+        const int g = plan_groups(table, stage_lds, ROT, b, groups, rt, c, extra, rw);
+        if (g < kStageGroups || c > (g + kStageGroups - 1) / kStageGroups) break;
+        if ((groups + g - 1) / g > (groups + ng - 1) / ng) break;
+        ks = c;
+        ng = g;
+      }
+    } else {
+      for (ks = kMaxWaves / rt; ks >= 1; --ks) {
+        ng = plan_groups(table, stage_lds, ROT, b, groups, rt, ks, extra, rw);
+        if (ng >= kStageGroups || ks == 1) break;
+      }
+    }
+    const int nst = (ng + kStageGroups - 1) / kStageGroups;
+    if (ks > nst) ks = nst;
+    if (ks < 1) ks = 1;
+    return Plan{rt, ks, ng, extra, rw, 0};
+  };
+  auto launches = [&](const Plan& p) { return p.ng >= 1 ? (groups + p.ng - 1) / p.ng : 1 << 30; };
+  Plan pl = plan(false, 8);
+  if (b > 1) {
+    const Plan px = plan(true, 8);
+    if (launches(px) < launches(pl) || (launches(px) == launches(pl) && pl.rt * pl.ks <= 8)) pl = px;
+  }
+  if (ROT && (pl.extra_waves || pl.rt * pl.ks >= 15)) {
+    const Plan p16 = plan(pl.extra_waves, kMaxRotWaves);
+    if (launches(p16) <= launches(pl) && p16.ks >= pl.ks) pl = p16;
+  }
+  return pl;
+}
+
+template <int PACKING, int NR, int XDT, bool ALIGNED, bool ROT>
+void launch_one(const uint8_t* packed, const uint16_t* scales, const void* xr, const uint32_t* sign_bits, float* y,
+                int b, int n, int k, hipStream_t s) {
+  const Plan pl = PACKING == 0 ? make_plan_2bit<ROT>(b, n, k) : make_plan<ROT>(PACKING, b, n, k);
+  if (pl.ng < 1) return;  // unreachable for batch <= 8 (room for >= 8 groups); never loop without progress
+  if constexpr (PACKING == 0) {
+    run_plan<0, NR, XDT, ALIGNED, ROT>(pl, packed, scales, xr, sign_bits, y, b, n, k, s);
+  } else {
+    if (pl.kind == 2) run_plan<2, NR, XDT, ALIGNED, ROT>(pl, packed, scales, xr, sign_bits, y, b, n, k, s);
+    else run_plan<1, NR, XDT, ALIGNED, ROT>(pl, packed, scales, xr, sign_bits, y, b, n, k, s);
   }
 }
 
