@@ -101,30 +101,13 @@ __host__ __device__ constexpr int f_region_bytes(int nb, int ng) {
   return f_bytes(nb, ng) + ((nb * e0_stride(ng) + 15) & ~15) + 16;
 }
 
-// K-slot of trit tau (0..127) of a group, and which matrix instruction of the
-// group it belongs to.  B operand: lane group q supplies slots 32q..32q+31.
-template <int PACK>
-__device__ __forceinline__ int slot_of(int tau, int* mi) {
-  if constexpr (PACK == 0) {
-    // dword w of lane group q: w=0 even / w=1 odd codes of bytes 8q..8q+3,
-    // w=2 / w=3 the same for bytes 8q+4..8q+7; nibble j = code 2j (+1).
-    const int q = tau >> 5, r = tau & 31;
-    const int w = ((r >> 4) << 1) | (r & 1);
-    *mi = 0;
-    return 32 * q + 8 * w + ((r & 15) >> 1);
-  } else {
-    // lane group q takes trits 30q .. 30q + 29 (bytes 6q .. 6q + 5) in its
-    // slots 0..29 and trits 120 + 2q, 121 + 2q (from bytes 24 and 25) in
-    // slots 30, 31
-    *mi = 0;
-    if (tau < 120) return 32 * (tau / 30) + tau % 30;
-    const int u = tau - 120;
-    return 32 * (u >> 1) + 30 + (u & 1);
-  }
-}
-
-// Trit (0..127) of a group that sits in K-slot s: the inverse of slot_of for
-// the base-3 layout.
+// Trit (0..127) of a group that sits in K-slot s of the base-3 layout.  B
+// operand lane group q supplies slots 32q .. 32q + 31: the trits of bytes
+// 6q .. 6q + 5 (trits 30q .. 30q + 29) in slots 0..29, and trits 120 + 2q,
+// 121 + 2q (from bytes 24 and 25) in slots 30, 31; the pad trits have none.
+// (2-bit codes need no map: dword w of lane group q holds the even (w even)
+// or odd codes of bytes 8q + 4 (w / 2) .., and the activations are stored in
+// that order by their own team layout.)
 __host__ __device__ constexpr int b3_tau_of_slot(int s) {
   return (s & 31) < 30 ? 30 * (s >> 5) + (s & 31) : 120 + 2 * (s >> 5) + ((s & 31) - 30);
 }
