@@ -395,11 +395,12 @@ def run_suite(path, argv):
                 rows.append((lin, packing, b, r))
                 print(f"{lin.name} {lin.n}x{lin.k} {packing} b{b}: fused {r['fused']:.2f} us, "
                       f"rotate {r['rotate']:.2f} + gemv {r['gemv']:.2f} us", flush=True)
-    # batches above 8 (chunks of 8 rows over the weights) on the FFN linear
+    # other batches on the FFN linear (above 8: tb_gemv in one pass, tb_linear
+    # in chunks of 8 rows)
     big = []
     gate = synth.BLOCK_LINEARS[4]
     for packing in ("2bit", "base3"):
-        for b in (2, 4, 16, 32):
+        for b in (2, 4, 9, 16, 32):
             r = suite_linear(packing, gate.n, gate.k, b, gen, steps=20)
             big.append((packing, b, r))
             print(f"gate {packing} b{b}: fused {r['fused']:.2f} us, gemv {r['gemv']:.2f} us", flush=True)
@@ -432,12 +433,14 @@ def run_suite(path, argv):
     lines.append("")
     lines.append("## Other batch sizes on gate (17408x5120)")
     lines.append("")
-    lines.append("Batches above 8 run as chunks of 8 rows, each streaming the weights again.")
+    lines.append("Above 8 rows, tb_gemv streams the weights once (fp16 matrix cores, gemv_wide.hip); "
+                 "tb_linear runs chunks of 8 rows, each streaming the weights again.")
     lines.append("")
-    lines.append("| packing | batch | tb_linear us | tb_gemv us | weight GB/s (tb_linear) |")
-    lines.append("|---|---|---|---|---|")
+    lines.append("| packing | batch | tb_linear us | tb_gemv us | weight GB/s (tb_linear) | weight GB/s (tb_gemv) |")
+    lines.append("|---|---|---|---|---|---|")
     for packing, b, r in big:
-        lines.append(f"| {packing} | {b} | {r['fused']:.2f} | {r['gemv']:.2f} | {r['bytes'] / (r['fused'] * 1e-6) / 1e9:.0f} |")
+        lines.append(f"| {packing} | {b} | {r['fused']:.2f} | {r['gemv']:.2f} | "
+                     f"{r['bytes'] / (r['fused'] * 1e-6) / 1e9:.0f} | {r['bytes'] / (r['gemv'] * 1e-6) / 1e9:.0f} |")
     lines.append("")
     lines.append("## Decode token stream: 64 layers, base-3, batch 1 (q/k/v and gate/up concatenated)")
     lines.append("")

@@ -11,7 +11,8 @@
 //     - sum_k x_k (the activation sum is kept per group).
 //   * base-3 bytes: one LDS table lookup turns a byte into a dword holding the
 //     nibbles of its five trits themselves (-1.0, 0, +1.0); the table has 32
-//     bank-spread copies so a wave's lookups do not conflict.  The 128 trits
+//     bank-spread copies so a wave's lookups do not conflict.  Per-row E8M0
+//     scales of the matrix instruction carry each A row's power of two.  The 128 trits
 //     of a group fill the 128 K-slots of one matrix instruction densely (the
 //     group's two pad trits are left out), so a group costs one instruction,
 //     as for 2-bit codes.
@@ -31,7 +32,11 @@
 // before it), go to a per-wave LDS buffer and are read back in the operand
 // layout.  A few "prep" waves turn the activations into
 // limbs in LDS (for as many groups as fit; larger K takes several launches)
-// while the other waves already stream weights.
+// while the other waves already stream weights; a launch may add waves that
+// only build limbs.  The host picks the plan per call (tiles per workgroup,
+// K-part waves, groups per launch, limb-only waves, rotation waves, and for
+// base-3 a 64 KB or a 32 KB decode table) from a rough cost per launch,
+// stage and prep pass.
 #include "tb_internal.hpp"
 
 #include <mutex>

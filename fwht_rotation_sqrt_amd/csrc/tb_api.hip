@@ -86,13 +86,19 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
 int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
             int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, void* stream) {
   if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
-  if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kGroup != 0 || !fits(N, K))
+  if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kGroup != 0 || !fits(N, K) ||
+      !fits(B, 4 * K))
     return TB_ERR_SHAPE;
   if (xr_dtype != TB_F32 && xr_dtype != TB_F16) return TB_ERR_DTYPE;
   if (N == 0) return TB_OK;
   if (!packed || !scales || !xr || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr) || !aligned16(y)) return TB_ERR_ALIGN;
-  // batches above the kernel's row sets run as chunks of rows
+  if (B >= tb::kWideMinBatch) {
+    // one pass over the weights on the fp16 matrix cores
+    tb::launch_gemv_wide(packing, packed, scales, xr, xr_dtype, y, int(B), int(N), int(K),
+                         static_cast<hipStream_t>(stream));
+    return finish_launch();
+  }
   const size_t xsz = xr_dtype == TB_F32 ? 4 : 2;
   for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
     const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;

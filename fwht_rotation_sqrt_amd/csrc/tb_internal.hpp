@@ -10,7 +10,9 @@ namespace tb {
 constexpr int kGroup = 128;          // weights per fp16 scale
 constexpr int kBlock = 1024;         // rotation block size
 constexpr int kB3GroupBytes = 26;    // base-3 bytes per 128-group (25 full bytes + 3 trits and 2 pads)
-constexpr int kMaxBatch = 8;         // largest decode batch
+constexpr int kMaxBatch = 8;         // largest batch of the limb decode product (gemv.hip)
+constexpr int kWideMinBatch = 9;     // from this batch on, tb_gemv runs gemv_wide.hip
+constexpr int kWideMaxBatch = 32;    // largest batch of gemv_wide.hip
 
 void launch_pack_2bit(const int8_t* trits, int64_t n, int64_t k, uint8_t* packed, int32_t* bad,
                       hipStream_t s);
@@ -22,6 +24,8 @@ void launch_fwht(const void* x, int x_dt, void* y, int y_dt, int64_t rows, int64
                  const uint32_t* sign_bits, hipStream_t s);
 void launch_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
                  int xr_dt, float* y, int b, int n, int k, hipStream_t s);
+void launch_gemv_wide(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr, int xr_dt,
+                      float* y, int b, int n, int k, hipStream_t s);
 void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y,
                  int m, int n, int k, hipStream_t s);
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,

@@ -49,9 +49,10 @@ typedef enum {
 typedef enum { TB_PACK_2BIT = 0, TB_PACK_BASE3 = 1 } tb_packing;
 typedef enum { TB_F32 = 0, TB_F16 = 1, TB_BF16 = 2 } tb_dtype;
 
-/* Largest batch tb_gemv and tb_linear accept.  Up to TB_GEMV_KERNEL_BATCH
- * rows run in one pass over the weights; a larger batch runs in chunks of
- * TB_GEMV_KERNEL_BATCH rows, each streaming the weights again. */
+/* Largest batch tb_gemv and tb_linear accept.  tb_gemv runs every batch in
+ * one pass over the weights.  tb_linear runs up to TB_GEMV_KERNEL_BATCH rows
+ * in one pass; a larger batch runs in chunks of TB_GEMV_KERNEL_BATCH rows,
+ * each streaming the weights again. */
 #define TB_GEMV_MAX_BATCH 32
 #define TB_GEMV_KERNEL_BATCH 8
 
@@ -110,8 +111,14 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
  * weight bytes streamed per token).
  * packed: [N][tb_packed_row_bytes(packing, K)]; scales: fp16 [N][K/128];
  * xr: [B][K] rotated activations of xr_dtype (TB_F32 or TB_F16), read as
- * given; y: fp32 [B][N], overwritten.  1 <= B <= TB_GEMV_MAX_BATCH (above
- * TB_GEMV_KERNEL_BATCH in chunks, see there).
+ * given; y: fp32 [B][N], overwritten.  1 <= B <= TB_GEMV_MAX_BATCH and
+ * B * K * 4 < 2^31.
+ * B <= TB_GEMV_KERNEL_BATCH: fp8 limbs of xr against fp4 codes, any
+ * magnitude (a power-of-two scale per row and 128-group).
+ * B > TB_GEMV_KERNEL_BATCH: fp16 matrix cores; fp32 xr is split into
+ * fp16 hi + lo (about 2^-21 of |x| lost), so |xr| must stay below 65504
+ * (larger values give inf or NaN), and values below 2^-14 keep an absolute
+ * error of at most 2^-24 instead of a relative one.
  * Accumulation is fp32 (not bit-reproducible across kernel versions). */
 int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
             int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, void* stream);

@@ -179,10 +179,12 @@ def test_gemv_ffn_base3_b1_end_to_end():
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("li", range(len(synth.BLOCK_LINEARS)), ids=[l.name for l in synth.BLOCK_LINEARS])
-def test_block_linears_b1_b8(packing, li):
+def test_block_linears_b1_b8_b32(packing, li):
+    """Every block linear at full size, batch 1 and 8 (limb kernel) and 32
+    (one-pass batched kernel for tb_gemv, chunks of 8 for tb_linear)."""
     lin = synth.BLOCK_LINEARS[li]
-    note(f"block linear {lin.name} {lin.n}x{lin.k} {packing} batch 1 and 8")
-    _e2e_gemv(2, packing, lin.n, lin.k, "bf16", False, (1, 8), 0, li)
+    note(f"block linear {lin.name} {lin.n}x{lin.k} {packing} batch 1, 8 and 32")
+    _e2e_gemv(2, packing, lin.n, lin.k, "bf16", False, (1, 8, 32), 0, li)
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
@@ -241,10 +243,62 @@ def test_gemv_extreme_magnitudes(packing, exp2):
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
+@pytest.mark.parametrize("n,k", [(1, 128), (16, 1024), (37, 1152), (300, 3200), (1000, 5120), (81, 17408),
+                                 (5000, 1024)])
+@pytest.mark.parametrize("xr_dtype", [torch.float32, torch.float16])
+def test_gemv_batches_9_to_32_one_pass(packing, n, k, xr_dtype):
+    """tb_gemv at 9..32 rows: one pass over the weights on the fp16 matrix
+    cores (one or two blocks of 16 rows, ragged row and column tails, 1..5
+    row tiles per workgroup, K split over the waves unevenly)."""
+    note(f"gemv wide {packing} n={n} k={k} xr={xr_dtype}")
+    g = synth.rng(222, 0, n % 251, k // 128)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    xr = g.standard_normal((tb.TB_GEMV_MAX_BATCH, k)).astype(np.float32)
+    if xr_dtype == torch.float16:
+        xr = xr.astype(np.float16)
+    packed, _ = PACK_REF[packing](t)
+    want = oracle.gemv(packing, packed, s, xr.astype(np.float64), k)
+    pd, sd, xd = dev(packed), scales_dev(s), dev(xr)
+    for b in (9, 16, 17, 21, tb.TB_GEMV_MAX_BATCH):
+        got = host(tb.tb_gemv(packing, pd, sd, xd[:b].contiguous()))
+        assert got.shape == (b, n)
+        err = oracle.rel_err(got, want[:b])
+        note(f"  b={b} rel err {err:.2e}")
+        assert err < TOL, (b, err)
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_gemv_batches_9_to_32_magnitudes(packing):
+    """The one-pass path carries fp32 x' as fp16 hi + lo: relative error
+    stays at the fp32 level up to |x'| near 65504 (largest value 60000), and
+    for tiny activations (|x'| ~ 2^-20, below the fp16 normal range) the
+    error per output stays within sum_k |s t| 2^-24."""
+    n, k = 300, 2048
+    note(f"gemv wide {packing} magnitudes")
+    g = synth.rng(223, 0, 0, 0)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    packed, _ = PACK_REF[packing](t)
+    pd, sd = dev(packed), scales_dev(s)
+    big = g.standard_normal((16, k))
+    big = (big * (60000.0 / np.abs(big).max())).astype(np.float32)
+    want = oracle.gemv(packing, packed, s, big.astype(np.float64), k)
+    got = host(tb.tb_gemv(packing, pd, sd, dev(big)))
+    assert oracle.rel_err(got, want) < 1e-5
+    tiny = np.ldexp(g.standard_normal((16, k)), -20).astype(np.float32)
+    want = oracle.gemv(packing, packed, s, tiny.astype(np.float64), k)
+    got = host(tb.tb_gemv(packing, pd, sd, dev(tiny)))
+    w = t.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    bound = np.abs(w).sum(axis=1) * 2.0 ** -24
+    assert np.all(np.abs(got - want) <= bound[None, :] * 1.01 + 1e-6 * np.abs(want))
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
 def test_gemv_linear_batches_above_8(packing):
-    """Batches above 8 run as chunks of 8 rows over the weights; every row
-    must match the oracle, across chunk boundaries and with a ragged last
-    chunk."""
+    """Batches above 8: tb_gemv takes them in one pass, tb_linear as chunks
+    of 8 rows over the weights; every row must match the oracle, across
+    chunk boundaries and with a ragged last chunk."""
     n, k = 200, 3072
     note(f"gemv/linear {packing} batches 9..32")
     g = synth.rng(260, 0, 0, 0)
@@ -271,15 +325,16 @@ def test_gemv_linear_batches_above_8(packing):
 def test_concatenated_linears_sampled_rows(packing, n):
     """q/k/v and gate/up as one call each (rows concatenated): 15360 and 34816
     rows of K = 5120, batch 1, 3 and 8, both entry points (34816 rows put 9
-    row tiles in a workgroup).  The oracle computes every 13th row and the
-    last 16 (the last, partial workgroup)."""
+    row tiles in a workgroup), and tb_gemv at 9 and 32 rows (one pass).  The
+    oracle computes every 13th row and the last 16 (the last, partial
+    workgroup)."""
     k = synth.HIDDEN
     note(f"concatenated linear {packing} {n}x{k}")
     g = synth.rng(270, 0, n % 251, 0)
     t = synth.trits(g, n, k)
     s = synth.scales_f16(g, n, k)
     signs = synth.sign_bits(g, k)
-    xbits = synth.f32_to_bf16_bits(g.standard_normal((8, k)).astype(np.float32))
+    xbits = synth.f32_to_bf16_bits(g.standard_normal((tb.TB_GEMV_MAX_BATCH, k)).astype(np.float32))
     x64 = synth.bf16_bits_to_f64(xbits)
     ref_packed, _ = PACK_REF[packing](t)
     rows = np.unique(np.concatenate([np.arange(0, n, 13), np.arange(n - 16, n)]))
@@ -290,6 +345,9 @@ def test_concatenated_linears_sampled_rows(packing, n):
     for b in (1, 3, 8):
         got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
         assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_linear", b)
+        got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
+        assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_gemv", b)
+    for b in (9, tb.TB_GEMV_MAX_BATCH):
         got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
         assert oracle.rel_err(got[:, rows], want[:b]) < TOL, ("tb_gemv", b)
 
