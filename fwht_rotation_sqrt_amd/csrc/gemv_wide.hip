@@ -51,9 +51,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;                    // waves per workgroup, splitting K
-// weight groups in flight per wave: one (two or three measured slower; the
-// kernel is bound by its VALU work, and the ring costs registers)
-__host__ __device__ constexpr int depth(int, int) { return 1; }
 constexpr uint32_t kCodeMask = 0x0C000C00u;  // bits 10-11 of both halves
 constexpr uint32_t kNegUnitPair = 0x84008400u;  // two fp16 -2^-14
 constexpr uint32_t kFar = 0x80000000u;       // buffer offset past any valid range: loads read 0
@@ -165,10 +162,10 @@ __device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c) {
 }
 
 // PACK: 0 = 2-bit codes, 1 = base-3 bytes.  MB: blocks of 16 activation rows.
-// T: tiles of 16 weight rows per workgroup.  NW: waves per workgroup.  DW:
-// groups of weights in flight per wave (a ring of register slots; the
-// activations of the next group are loaded one group ahead).
-template <int PACK, int XF32, int MB, int T, int NW, int DW>
+// T: tiles of 16 weight rows per workgroup.  NW: waves per workgroup.  The
+// weights and activations of the next group are loaded while this one
+// computes (one register slot per tile).
+template <int PACK, int XF32, int MB, int T, int NW>
 __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const void* __restrict__ xr, float* __restrict__ y,
@@ -190,29 +187,33 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   // per-lane offsets of group 0; rows past n and activation rows past nb
   // fall outside their buffers and read zero, and so does every group at or
   // past g1 (group kPastGroups, activation offset kFar)
+  // (tile t adds t times a wave-uniform stride, so only tile 0's offsets
+  // take vector registers)
   const int tile0 = blockIdx.x * T;
-  uint32_t wbase[T], sbase[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const uint32_t row = uint32_t(16 * (tile0 + t) + r);
-    wbase[t] = row * row_bytes + uint32_t(PACK == 0 ? 8 * q : 6 * q);
-    sbase[t] = row * uint32_t(groups) * 2u;
-  }
+  const uint32_t row0 = uint32_t(16 * tile0 + r);
+  const uint32_t wbase = row0 * row_bytes + uint32_t(PACK == 0 ? 8 * q : 6 * q), wstride = 16u * row_bytes;
+  const uint32_t sbase = row0 * uint32_t(groups) * 2u, sstride = 32u * uint32_t(groups);
   uint32_t xbase[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) xbase[mb] = (uint32_t(16 * mb + r) * uint32_t(k) + uint32_t(32 * q)) * kXsz;
 
-  u32x2 wr[DW][T];
-  uint32_t sr[DW][T];
+  u32x2 wr[T];
+  uint32_t sr[T];
   ARaw<XF32> an[MB];
-  auto issue_w = [&](int d, int g) {
-    // group kPastGroups lies past the end of both buffers for every row
-    const uint32_t gg = g < g1 ? uint32_t(g) : kPastGroups;
+  // group kPastGroups lies past the end of both buffers for every row
+  auto group_or_past = [&](int g) { return g < g1 ? uint32_t(g) : kPastGroups; };
+  // with few tiles the per-tile offsets stay in registers
+  uint32_t wb[T], sb[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      wr[d][t] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wbase[t] + gg * kGroupBytes, 0, 0);
-      sr[d][t] = __builtin_amdgcn_raw_buffer_load_b16(srs, sbase[t] + 2u * gg, 0, 0);
-    }
+  for (int t = 0; t < T; ++t) {
+    wb[t] = wbase + uint32_t(t) * wstride;
+    sb[t] = sbase + uint32_t(t) * sstride;
+  }
+  auto issue_w = [&](int t, uint32_t gg) {
+    const uint32_t wo = T <= 3 ? wb[t] : wbase + uint32_t(t) * wstride;
+    const uint32_t so = T <= 3 ? sb[t] : sbase + uint32_t(t) * sstride;
+    wr[t] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wo + gg * kGroupBytes, 0, 0);
+    sr[t] = __builtin_amdgcn_raw_buffer_load_b16(srs, so + 2u * gg, 0, 0);
   };
   auto issue_a = [&](int g) {
     const bool ok = g < g1;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   };
   // the first groups' loads go out before the table is built
 #pragma unroll
-  for (int d = 0; d < DW; ++d) issue_w(d, g0 + d);
+  for (int t = 0; t < T; ++t) issue_w(t, group_or_past(g0));
   issue_a(g0);
 
   const uint32_t tab = 4u * uint32_t(lane & 31);
@@ -243,61 +244,61 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const u32x4 neg_unit = u32x4{kNegUnitPair, kNegUnitPair, kNegUnitPair, kNegUnitPair};
-  for (int gb = g0; gb < g1; gb += DW) {
+  for (int g = g0; g < g1; ++g) {
+    ARaw<XF32> ac[MB];
 #pragma unroll
-    for (int d = 0; d < DW; ++d) {
-      const int g = gb + d;
-      u32x2 wc[T];
-      uint32_t sc[T];
-      ARaw<XF32> ac[MB];
+    for (int mb = 0; mb < MB; ++mb) ac[mb] = an[mb];
+    const uint32_t gn = group_or_past(g + 1);
+    // With few tiles a group's work is short, so the next group's weights go
+    // out now; with many, each tile's go out after its decode (registers).
+    constexpr bool kEarly = T <= 3;
+    u32x2 wc[T];
+    uint32_t sc[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        wc[t] = wr[d][t];
-        sc[t] = sr[d][t];
+    for (int t = 0; t < T; ++t) {
+      wc[t] = wr[t];
+      sc[t] = sr[t];
+      if constexpr (kEarly) issue_w(t, gn);
+    }
+    issue_a(g + 1);  // past g1 it reads zero
+
+    // activation operands and the group's -2^-14 sum_k x'
+    u32x4 ahi[MB][4], alo[MB][4];
+    floatx4 neg_sum[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      a_operands<XF32>(ac[mb], ahi[mb], alo[mb]);
+      neg_sum[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        neg_sum[mb] = mfma(ahi[mb][j], neg_unit, neg_sum[mb]);
+        if constexpr (XF32) neg_sum[mb] = mfma(alo[mb][j], neg_unit, neg_sum[mb]);
       }
+    }
+
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) ac[mb] = an[mb];
-      // refill: this slot takes group g + DW, the activations group g + 1
-      // (issued on every path, so the memory-counter waits stay exact)
-      issue_w(d, g + DW);
-      issue_a(g + 1);
-      if (g < g1) {
-        // activation operands and the group's -2^-14 sum_k x'
-        u32x4 ahi[MB][4], alo[MB][4];
-        floatx4 neg_sum[MB];
+    for (int t = 0; t < T; ++t) {
+      u32x2 w = wc[t];
+      const uint32_t sbits = sc[t];
+      if constexpr (PACK == 1) w = base3_word(w, tab, 4u * uint32_t(q));
+      u32x4 b[4];
+      b_operands(w, b);
+      if constexpr (!kEarly) issue_w(t, gn);  // this tile's next group
+      floatx4 part[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) part[mb] = neg_sum[mb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          a_operands<XF32>(ac[mb], ahi[mb], alo[mb]);
-          neg_sum[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            neg_sum[mb] = mfma(ahi[mb][j], neg_unit, neg_sum[mb]);
-            if constexpr (XF32) neg_sum[mb] = mfma(alo[mb][j], neg_unit, neg_sum[mb]);
-          }
+          part[mb] = mfma(ahi[mb][j], b[j], part[mb]);
+          if constexpr (XF32) part[mb] = mfma(alo[mb][j], b[j], part[mb]);
         }
+      const float s = 16384.f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sbits)));
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          u32x2 w = wc[t];
-          if constexpr (PACK == 1) w = base3_word(w, tab, 4u * uint32_t(q));
-          u32x4 b[4];
-          b_operands(w, b);
-          floatx4 part[MB];
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) part[mb] = neg_sum[mb];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              part[mb] = mfma(ahi[mb][j], b[j], part[mb]);
-              if constexpr (XF32) part[mb] = mfma(alo[mb][j], b[j], part[mb]);
-            }
-          const float s = 16384.f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sc[t])));
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(s, part[mb][i], acc[t][mb][i]);
-        }
-      }
+        for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(s, part[mb][i], acc[t][mb][i]);
     }
   }
 
@@ -323,16 +324,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
 
 template <int PACK, int XF32, int MB, int T>
 void run(const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k, hipStream_t s) {
-  constexpr int NW = kWaves, DW = depth(XF32, MB);
+  constexpr int NW = kWaves;
   constexpr int lds = (PACK == 1 ? kTableBytes : 0) + NW * T * MB * kRedSlot;
   static const bool attr = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_wide_kernel<PACK, XF32, MB, T, NW, DW>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_wide_kernel<PACK, XF32, MB, T, NW>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     return true;
   }();
   (void)attr;
   const int tiles = (n + 15) / 16;
-  gemv_wide_kernel<PACK, XF32, MB, T, NW, DW><<<(tiles + T - 1) / T, 64 * NW, lds, s>>>(p, sc, x, y, b, n, k);
+  gemv_wide_kernel<PACK, XF32, MB, T, NW><<<(tiles + T - 1) / T, 64 * NW, lds, s>>>(p, sc, x, y, b, n, k);
 }
 
 template <int PACK, int XF32, int MB>
