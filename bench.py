@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating HBM byte counters) and exit")
+    ap.add_argument("--gemv-batch", type=int, metavar="B",
+                    help="instead of the one-line record: time tb_gemv alone on the FFN gate/up linear "
+                         "(base-3 17408x5120) at batch B, cache-cold, and print one JSON line")
     ap.add_argument("--suite", metavar="OUT_MD",
                     help="instead of the one-line record: time the block linears (both packings, batch 1 and 8), "
                          "the 64-layer decode token stream and a 2 GiB read, and write a markdown summary")
@@ -469,6 +472,35 @@ def run_suite(path, argv):
           flush=True)
 
 
+def bench_gemv_batch(b, steps):
+    """tb_gemv alone at batch b on gate/up (base-3 17408x5120), weights cycled
+    through > 512 MB of copies, fp32 x' ~ N(0,1); us per call from HIP events
+    over a graph of `steps` calls."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(SUITE_SEED)
+    gate = synth.BLOCK_LINEARS[4]
+    n, k = gate.n, gate.k
+    p0, s0 = gpu_packed("base3", n, k, gen)
+    per = p0.numel() + 2 * s0.numel()
+    copies = max(2, -(-CACHE_BYTES // per))
+    ps = [p0] + [p0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    xr = torch.randn((b, k), device="cuda", generator=gen)
+    y = torch.empty((b, n), dtype=torch.float32, device="cuda")
+
+    def gemv():
+        for i in range(steps):
+            tb.tb_gemv("base3", ps[i % copies], ss[i % copies], xr, y=y)
+
+    _, g = time_graph(gemv, gemv)
+    us = event_time(g, 3) / steps * 1e6
+    return {"metric": "tb_gemv weight GB/s (codes + scales read once per call)", "value": round(per / us / 1e3, 2),
+            "unit": "GB/s", "us_per_call": round(us, 3), "batch": b,
+            "kernel": "gemv_wide_kernel (fp16 matrix cores)" if b > tb.TB_GEMV_KERNEL_BATCH else "gemv_mfma_kernel (fp8 limbs)",
+            "config": {"workload": f"gemv_gate_{n}x{k}_base3_b{b}", "n": n, "k": k, "packing": "base3",
+                       "bytes_per_call": per, "weight_copies": copies, "x_dtype": "f32"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -488,6 +520,9 @@ def main():
     tb.library()
     if args.suite:
         run_suite(args.suite, sys.argv[1:])
+        return
+    if args.gemv_batch:
+        print(json.dumps(bench_gemv_batch(args.gemv_batch, args.steps)), flush=True)
         return
     d = decode_setup()
     wall, t_fused, t_gemv, t_rot = bench_decode(d, args.steps, args.warmup)

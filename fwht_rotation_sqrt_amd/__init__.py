@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libtb.so")
 
 TB_PACK_2BIT, TB_PACK_BASE3 = 0, 1
 TB_F32, TB_F16, TB_BF16 = 0, 1, 2
-TB_GEMV_MAX_BATCH = 32   # batches above 8 run in chunks of 8 rows, each re-streaming the weights
+TB_GEMV_MAX_BATCH = 32   # tb_gemv: one pass over the weights at any batch up to this
+TB_GEMV_KERNEL_BATCH = 8  # tb_linear above this: chunks of 8 rows, each re-streaming the weights
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",

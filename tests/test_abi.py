@@ -86,6 +86,8 @@ def test_gemv_validation():
     assert g(0, P, P, P, 0, P, tb.TB_GEMV_MAX_BATCH + 1, 8, 128, None) == SHAPE
     assert g(0, P, P, P, 0, P, 1, 8, 192, None) == SHAPE
     assert g(0, P, P, P, 0, P, 1, -8, 128, None) == SHAPE
+    # 32 rows of K = 2^26 fp32 activations are 2^33 bytes: past the 32-bit offsets
+    assert g(0, P, P, P, 0, P, 32, 8, 1 << 26, None) == SHAPE
     assert g(0, P, P, P, 2, P, 1, 8, 128, None) == DTYPE
     assert g(1, None, P, P, 0, P, 1, 8, 128, None) == NULL
     assert g(1, P, None, P, 0, P, 1, 8, 128, None) == NULL
