@@ -135,6 +135,17 @@ int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const ui
   if (M == 0 || N == 0) return TB_OK;
   if (!packed || !scales || !xr_f16 || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr_f16) || !aligned16(y)) return TB_ERR_ALIGN;
+  if (M <= tb::kWideGemmRows && fits(tb::kWideMaxBatch, 2 * K)) {
+    // few rows: chunks of up to 32 rows on the batched decode kernel, each
+    // streaming the weights once over the whole grid, where the GEMM's
+    // 128-row tiles would leave most of the chip idle
+    for (int64_t m0 = 0; m0 < M; m0 += tb::kWideMaxBatch) {
+      const int64_t mc = M - m0 < tb::kWideMaxBatch ? M - m0 : tb::kWideMaxBatch;
+      tb::launch_gemv_wide(packing, packed, scales, xr_f16 + m0 * K, TB_F16, y + m0 * N, int(mc), int(N),
+                           int(K), static_cast<hipStream_t>(stream));
+    }
+    return finish_launch();
+  }
   tb::launch_gemm(packing, packed, scales, xr_f16, y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
   return finish_launch();
 }

@@ -13,6 +13,7 @@ constexpr int kB3GroupBytes = 26;    // base-3 bytes per 128-group (25 full byte
 constexpr int kMaxBatch = 8;         // largest batch of the limb decode product (gemv.hip)
 constexpr int kWideMinBatch = 9;     // from this batch on, tb_gemv runs gemv_wide.hip
 constexpr int kWideMaxBatch = 32;    // largest batch of gemv_wide.hip
+constexpr int kWideGemmRows = 96;    // tb_gemm up to this M runs gemv_wide.hip in chunks of 32 rows
 
 void launch_pack_2bit(const int8_t* trits, int64_t n, int64_t k, uint8_t* packed, int32_t* bad,
                       hipStream_t s);

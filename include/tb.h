@@ -145,7 +145,10 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
  * as written by tb_pack_2bit / tb_pack_base3 (any address alignment for base-3
  * rows is handled; the buffer itself 16-byte aligned); scales [N][K/128].
  * xr_f16: fp16 [M][K]; y: fp32 [M][N], overwritten.  Products t*s are exact in
- * fp16; accumulation is fp32 on the matrix cores.  K % 128 == 0. */
+ * fp16; accumulation is fp32 on the matrix cores.  K % 128 == 0.
+ * M <= 96 runs as chunks of up to 32 rows on the batched decode kernel of
+ * tb_gemv (one pass over the weights per chunk); larger M on 128 x 272
+ * output tiles. */
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream);
 

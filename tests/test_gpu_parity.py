@@ -356,7 +356,8 @@ def test_concatenated_linears_sampled_rows(packing, n):
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 37, 1024), (64, 64, 256), (100, 300, 2048), (130, 1000, 5120),
-                                   (129, 545, 1152), (7, 273, 640)])
+                                   (129, 545, 1152), (7, 273, 640), (32, 300, 2048), (33, 300, 2048),
+                                   (96, 300, 2048), (97, 300, 2048), (16, 17408, 5120)])
 def test_gemm_small_shapes(packing, m, n, k):
     note(f"gemm {packing} m={m} n={n} k={k}")
     g = synth.rng(230, 0, m % 251, n % 251)
@@ -394,6 +395,11 @@ def test_gemm_base3_equals_2bit():
     t = synth.trits(g, n, k)
     s = scales_dev(synth.scales_f16(g, n, k))
     xr = dev(g.standard_normal((m, k)).astype(np.float16))
-    y2 = host(tb.tb_gemm("2bit", dev(oracle.pack_2bit(t)[0]), s, xr))
-    y3 = host(tb.tb_gemm("base3", dev(oracle.pack_base3(t)[0]), s, xr))
+    p2, p3 = dev(oracle.pack_2bit(t)[0]), dev(oracle.pack_base3(t)[0])
+    y2 = host(tb.tb_gemm("2bit", p2, s, xr))
+    y3 = host(tb.tb_gemm("base3", p3, s, xr))
+    assert np.array_equal(y2, y3)
+    # a few rows run on the batched decode kernel: the same holds there
+    y2 = host(tb.tb_gemm("2bit", p2, s, xr[:20].contiguous()))
+    y3 = host(tb.tb_gemm("base3", p3, s, xr[:20].contiguous()))
     assert np.array_equal(y2, y3)
