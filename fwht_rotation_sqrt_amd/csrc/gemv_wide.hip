@@ -184,11 +184,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   const int per_wave = (groups + NW - 1) / NW;
   const int g0 = min(groups, wave * per_wave), g1 = min(groups, g0 + per_wave);
 
-  // per-lane offsets of group 0; rows past n and activation rows past nb
+  // Per-lane offsets of group 0.  Rows past n and activation rows past nb
   // fall outside their buffers and read zero, and so does every group at or
-  // past g1 (group kPastGroups, activation offset kFar)
-  // (tile t adds t times a wave-uniform stride, so only tile 0's offsets
-  // take vector registers)
+  // past g1 (group kPastGroups, activation offset kFar).  Tile t lies t
+  // wave-uniform strides further; with up to 3 tiles the T offsets are kept
+  // in registers, with more they are recomputed at each load (registers).
+  constexpr bool kEarly = T <= 3;  // also: all next-group weight loads at the group start
   const int tile0 = blockIdx.x * T;
   const uint32_t row0 = uint32_t(16 * tile0 + r);
   const uint32_t wbase = row0 * row_bytes + uint32_t(PACK == 0 ? 8 * q : 6 * q), wstride = 16u * row_bytes;
@@ -202,7 +203,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   ARaw<XF32> an[MB];
   // group kPastGroups lies past the end of both buffers for every row
   auto group_or_past = [&](int g) { return g < g1 ? uint32_t(g) : kPastGroups; };
-  // with few tiles the per-tile offsets stay in registers
   uint32_t wb[T], sb[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -210,8 +210,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
     sb[t] = sbase + uint32_t(t) * sstride;
   }
   auto issue_w = [&](int t, uint32_t gg) {
-    const uint32_t wo = T <= 3 ? wb[t] : wbase + uint32_t(t) * wstride;
-    const uint32_t so = T <= 3 ? sb[t] : sbase + uint32_t(t) * sstride;
+    const uint32_t wo = kEarly ? wb[t] : wbase + uint32_t(t) * wstride;
+    const uint32_t so = kEarly ? sb[t] : sbase + uint32_t(t) * sstride;
     wr[t] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wo + gg * kGroupBytes, 0, 0);
     sr[t] = __builtin_amdgcn_raw_buffer_load_b16(srs, so + 2u * gg, 0, 0);
   };
@@ -251,7 +251,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
     const uint32_t gn = group_or_past(g + 1);
     // With few tiles a group's work is short, so the next group's weights go
     // out now; with many, each tile's go out after its decode (registers).
-    constexpr bool kEarly = T <= 3;
     u32x2 wc[T];
     uint32_t sc[T];
 #pragma unroll
