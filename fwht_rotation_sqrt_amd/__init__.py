@@ -85,6 +85,49 @@ def _check(t: torch.Tensor, name: str, dtypes) -> None:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
 
 
+def _shape(t: torch.Tensor, name: str, want) -> None:
+    """Exact shape check before any launch: the kernels size their reads and
+    writes from the integer arguments, not from the tensors."""
+    if tuple(t.shape) != tuple(int(w) for w in want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(w) for w in want)}")
+
+
+def _rank2(t: torch.Tensor, name: str) -> None:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+
+
+def _row_bytes(packing, k: int) -> int:
+    rb = tb_packed_row_bytes(packing, k)
+    if rb < 0:
+        raise ValueError(f"K = {k} is not a positive multiple of 128 (or the packing is unknown)")
+    return rb
+
+
+def _weights(packing, packed, scales, k: int) -> int:
+    """Check packed [N][row bytes] and scales [N][K/128]; return N."""
+    _check(packed, "packed", (torch.uint8,))
+    _check(scales, "scales", (torch.float16,))
+    _rank2(packed, "packed")
+    n = packed.shape[0]
+    _shape(packed, "packed", (n, _row_bytes(packing, k)))
+    _shape(scales, "scales", (n, k // 128))
+    return n
+
+
+def _signs(sign_bits: torch.Tensor, k: int) -> None:
+    _check(sign_bits, "sign_bits", (torch.int32,))
+    if sign_bits.dim() != 1 or sign_bits.numel() != k // 32:
+        raise ValueError(f"sign_bits must hold K/32 = {k // 32} int32 words, got shape {tuple(sign_bits.shape)}")
+
+
+def _count(bad_count) -> None:
+    if bad_count is not None:
+        _check(bad_count, "bad_count", (torch.int32,))
+        if bad_count.numel() < 1:
+            raise ValueError("bad_count must hold at least one int32")
+
+
 def _call(name: str, *args) -> None:
     st = getattr(library(), name)(*args)
     if st != 0:
@@ -105,15 +148,14 @@ def tb_packed_row_bytes(packing, k: int) -> int:
 
 def _pack(name, packing, trits, packed, bad_count, stream):
     _check(trits, "trits", (torch.int8,))
+    _rank2(trits, "trits")
     n, k = trits.shape
-    rb = tb_packed_row_bytes(packing, k)
-    if rb < 0:
-        raise ValueError("K must be a positive multiple of 128")
+    rb = _row_bytes(packing, k)
     if packed is None:
         packed = torch.empty((n, rb), dtype=torch.uint8, device=trits.device)
     _check(packed, "packed", (torch.uint8,))
-    if bad_count is not None:
-        _check(bad_count, "bad_count", (torch.int32,))
+    _shape(packed, "packed", (n, rb))
+    _count(bad_count)
     _call(name, _ptr(trits), n, k, _ptr(packed), _ptr(bad_count), _stream(stream))
     return packed
 
@@ -131,12 +173,14 @@ def tb_pack_base3(trits, packed=None, bad_count=None, stream=None):
 def tb_unpack(packing, packed, k: int, trits=None, bad_count=None, stream=None):
     """Packed codes -> int8 [N][K] trits."""
     _check(packed, "packed", (torch.uint8,))
-    n = packed.shape[0]
+    _rank2(packed, "packed")
+    n, k = packed.shape[0], int(k)
+    _shape(packed, "packed", (n, _row_bytes(packing, k)))
     if trits is None:
         trits = torch.empty((n, k), dtype=torch.int8, device=packed.device)
     _check(trits, "trits", (torch.int8,))
-    if bad_count is not None:
-        _check(bad_count, "bad_count", (torch.int32,))
+    _shape(trits, "trits", (n, k))
+    _count(bad_count)
     _call("tb_unpack", _packing(packing), _ptr(packed), n, int(k), _ptr(trits), _ptr(bad_count),
           _stream(stream))
     return trits
@@ -145,11 +189,13 @@ def tb_unpack(packing, packed, k: int, trits=None, bad_count=None, stream=None):
 def tb_fwht_rotate(x, sign_bits, out_dtype=torch.float32, out=None, stream=None):
     """[rows][K] activations -> R_K x as fp32 or fp16."""
     _check(x, "x", tuple(_ACT_DT))
-    _check(sign_bits, "sign_bits", (torch.int32,))
+    _rank2(x, "x")
     rows, k = x.shape
+    _signs(sign_bits, k)
     if out is None:
         out = torch.empty((rows, k), dtype=out_dtype, device=x.device)
     _check(out, "out", (torch.float32, torch.float16))
+    _shape(out, "out", (rows, k))
     _call("tb_fwht_rotate", _ptr(x), _ACT_DT[x.dtype], _ptr(out), _ACT_DT[out.dtype], rows, k,
           _ptr(sign_bits), _stream(stream))
     return out
@@ -157,14 +203,14 @@ def tb_fwht_rotate(x, sign_bits, out_dtype=torch.float32, out=None, stream=None)
 
 def tb_gemv(packing, packed, scales, xr, y=None, stream=None):
     """y[B][N] = packed ternary W (g128 fp16 scales) times rotated activations xr[B][K]."""
-    _check(packed, "packed", (torch.uint8,))
-    _check(scales, "scales", (torch.float16,))
     _check(xr, "xr", (torch.float32, torch.float16))
+    _rank2(xr, "xr")
     b, k = xr.shape
-    n = packed.shape[0]
+    n = _weights(packing, packed, scales, k)
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=xr.device)
     _check(y, "y", (torch.float32,))
+    _shape(y, "y", (b, n))
     _call("tb_gemv", _packing(packing), _ptr(packed), _ptr(scales), _ptr(xr), _ACT_DT[xr.dtype],
           _ptr(y), b, n, k, _stream(stream))
     return y
@@ -172,15 +218,15 @@ def tb_gemv(packing, packed, scales, xr, y=None, stream=None):
 
 def tb_linear(packing, packed, scales, x, sign_bits, y=None, stream=None):
     """y[B][N] = packed ternary W times R_K x, x[B][K] unrotated (rotation inside the call)."""
-    _check(packed, "packed", (torch.uint8,))
-    _check(scales, "scales", (torch.float16,))
     _check(x, "x", tuple(_ACT_DT))
-    _check(sign_bits, "sign_bits", (torch.int32,))
+    _rank2(x, "x")
     b, k = x.shape
-    n = packed.shape[0]
+    n = _weights(packing, packed, scales, k)
+    _signs(sign_bits, k)
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=x.device)
     _check(y, "y", (torch.float32,))
+    _shape(y, "y", (b, n))
     _call("tb_linear", _packing(packing), _ptr(packed), _ptr(scales), _ptr(x), _ACT_DT[x.dtype],
           _ptr(sign_bits), _ptr(y), b, n, k, _stream(stream))
     return y
@@ -188,14 +234,14 @@ def tb_linear(packing, packed, scales, x, sign_bits, y=None, stream=None):
 
 def tb_gemm(packing, packed, scales, xr, y=None, stream=None):
     """Y[M][N] = X'[M][K] (fp16) times the packed ternary weights, fp32 out."""
-    _check(packed, "packed", (torch.uint8,))
-    _check(scales, "scales", (torch.float16,))
     _check(xr, "xr", (torch.float16,))
+    _rank2(xr, "xr")
     m, k = xr.shape
-    n = packed.shape[0]
+    n = _weights(packing, packed, scales, k)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=xr.device)
     _check(y, "y", (torch.float32,))
+    _shape(y, "y", (m, n))
     _call("tb_gemm", _packing(packing), _ptr(packed), _ptr(scales), _ptr(xr), _ptr(y), m, n, k,
           _stream(stream))
     return y

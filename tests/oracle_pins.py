@@ -339,6 +339,66 @@ def pin_gemm_rows_are_gemv(o, read_golden=None):
         assert np.max(np.abs(y[r] - yr)) <= 1e-13 * np.max(np.abs(yr))
 
 
+# ------------------------------------------------------------------ comparison metric
+#
+# Every product parity verdict goes through rel_err: e = max_i |y_i - yref_i| /
+# max(|yref_i|, rms of yref's row), the reading of the "max relative error 2e-3"
+# bound in which an output that cancels to near zero is measured against its
+# row's rms.  The cases below are small enough to work out by hand.
+
+def pin_rel_err_hand_cases(o, read_golden=None):
+    # one row, floor active: rms([3, 4, 0]) = sqrt(25/3); the error sits on the 0
+    e = o.rel_err(np.array([[3.0, 4.0, 0.01]]), np.array([[3.0, 4.0, 0.0]]))
+    assert abs(e - 0.01 / np.sqrt(25 / 3)) < 1e-15
+    # floor inactive: |yref| = 4 > rms, so the error is relative to 4
+    e = o.rel_err(np.array([[3.0, 4.004, 0.0]]), np.array([[3.0, 4.0, 0.0]]))
+    assert abs(e - 0.004 / 4) < 1e-15
+    # the rms is per row: a small row is not floored by a large row's rms
+    yref = np.array([[1000.0, -1000.0], [1.0, 1.0]])
+    y = np.array([[1000.0, -1000.0], [1.002, 1.0]])
+    assert abs(o.rel_err(y, yref) - 0.002) < 1e-12
+    # maximum, not mean, over the elements
+    yref = np.ones((1, 4))
+    y = np.array([[1.002, 1.0, 1.0, 1.0]])
+    assert abs(o.rel_err(y, yref) - 0.002) < 1e-12
+    # the denominator is the reference's, not the candidate's
+    y = np.array([[1.0, 1.0, 1.0, 11.0]])
+    assert o.rel_err(y, yref) == 10.0
+    # a reference exactly 0 next to a non-zero entry: the floor is rms = sqrt(2)
+    e = o.rel_err(np.array([[1e-3, 2.0]]), np.array([[0.0, 2.0]]))
+    assert abs(e - 1e-3 / np.sqrt(2)) < 1e-15
+    # leading dimensions are rows: [2][1][3] is two rows of three
+    yref = np.array([[[3.0, 4.0, 0.0]], [[300.0, 400.0, 0.0]]])
+    y = yref.copy()
+    y[1, 0, 2] = 1.0
+    assert abs(o.rel_err(y, yref) - 1.0 / np.sqrt(250000 / 3)) < 1e-15
+    # an all-zero reference row: the error is absolute
+    assert o.rel_err(np.array([[0.5, 0.0]]), np.zeros((1, 2))) == 0.5
+    assert o.rel_err(np.zeros((1, 2)), np.zeros((1, 2))) == 0.0
+    # exact agreement and the empty call
+    assert o.rel_err(yref, yref) == 0.0
+    assert o.rel_err(np.zeros((0, 5)), np.zeros((0, 5))) == 0.0
+    # non-finite outputs never pass a bound
+    for bad in (np.nan, np.inf, -np.inf):
+        y = np.ones((1, 4))
+        y[0, 2] = bad
+        e = o.rel_err(y, np.ones((1, 4)))
+        assert not (e < 1e30)
+
+
+def pin_normwise_err_hand_cases(o, read_golden=None):
+    # |(3, 4.5) - (3, 4)| / |(3, 4)| = 0.5 / 5
+    assert abs(o.normwise_err(np.array([3.0, 4.5]), np.array([3.0, 4.0])) - 0.1) < 1e-15
+    # over the whole array, not row by row: |(0, 0, 0, 0.1)| / |(3, 4, 0.3, 0.4)|
+    y = np.array([[3.0, 4.0], [0.3, 0.5]])
+    yref = np.array([[3.0, 4.0], [0.3, 0.4]])
+    assert abs(o.normwise_err(y, yref) - 0.1 / np.sqrt(25.25)) < 1e-14
+    # a zero reference gives the norm of y itself
+    assert o.normwise_err(np.array([3.0, 4.0]), np.zeros(2)) == 5.0
+    y = np.array([1.0, np.nan])
+    assert not (o.normwise_err(y, np.ones(2)) < 1e30)
+
+
 ALL_PINS = [
     pin_base3_page_example, pin_base3_bijection, pin_base3_pad_and_size, pin_base3_bad_counts,
     pin_2bit_base4_number, pin_2bit_bijection, pin_2bit_bad_counts, pin_bits_per_weight,
@@ -346,4 +406,5 @@ ALL_PINS = [
     pin_rotation_closed_forms, pin_rotation_butterfly, pin_rotation_inverse,
     pin_gemv_bruteforce, pin_gemv_associativity, pin_gemv_unit_inputs,
     pin_gemv_zero_and_linearity, pin_gemm_rows_are_gemv,
+    pin_rel_err_hand_cases, pin_normwise_err_hand_cases,
 ]

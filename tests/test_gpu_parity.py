@@ -357,7 +357,9 @@ def test_concatenated_linears_sampled_rows(packing, n):
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 37, 1024), (64, 64, 256), (100, 300, 2048), (130, 1000, 5120),
                                    (129, 545, 1152), (7, 273, 640), (32, 300, 2048), (33, 300, 2048),
-                                   (96, 300, 2048), (97, 300, 2048), (16, 17408, 5120)])
+                                   (96, 300, 2048), (97, 300, 2048), (16, 17408, 5120),
+                                   # M > 96 runs on the 128 x 272 tiles: K loops of 1, 2 and 5 groups
+                                   (97, 300, 128), (130, 290, 256), (200, 17, 640)])
 def test_gemm_small_shapes(packing, m, n, k):
     note(f"gemm {packing} m={m} n={n} k={k}")
     g = synth.rng(230, 0, m % 251, n % 251)
@@ -391,7 +393,7 @@ def test_gemm_pp512_end_to_end(packing):
 def test_gemm_base3_equals_2bit():
     note("gemm base-3 and 2-bit of the same trits agree exactly")
     g = synth.rng(231, 0, 0, 0)
-    m, n, k = 96, 300, 1280
+    m, n, k = 130, 300, 1280      # M > 96: the tiled prefill kernel
     t = synth.trits(g, n, k)
     s = scales_dev(synth.scales_f16(g, n, k))
     xr = dev(g.standard_normal((m, k)).astype(np.float16))

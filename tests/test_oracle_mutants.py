@@ -74,6 +74,38 @@ def _pack3_pad_first(orig, trits):
     return (d * o.POW3).sum(-1).reshape(n, -1).astype(np.uint8), bad
 
 
+def _rel_err_variant(mean=False, global_rms=False, cand_den=False, no_floor=False):
+    def fn(orig, y, yref):
+        y = np.asarray(y, dtype=np.float64)
+        yref = np.asarray(yref, dtype=np.float64)
+        yr = yref.reshape(-1, yref.shape[-1])
+        yc = y.reshape(yr.shape)
+        if not yr.size:
+            return 0.0
+        if global_rms:
+            rms = np.sqrt(np.mean(yr * yr))
+        else:
+            rms = np.sqrt(np.mean(yr * yr, axis=1, keepdims=True))
+        mag = np.abs(yc) if cand_den else np.abs(yr)
+        den = mag if no_floor else np.maximum(mag, rms)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.abs(yc - yr) / np.where(den == 0, 1.0, den)
+        return float(np.mean(ratio) if mean else np.max(ratio))
+    return fn
+
+
+def _normwise_per_row_max(orig, y, yref):
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    yref = np.atleast_2d(np.asarray(yref, dtype=np.float64))
+    d = np.linalg.norm(yref, axis=-1)
+    num = np.linalg.norm(y - yref, axis=-1)
+    return float(np.max(np.where(d > 0, num / np.where(d > 0, d, 1), num)))
+
+
+def _normwise_no_division(orig, y, yref):
+    return float(np.linalg.norm(np.asarray(y, float) - np.asarray(yref, float)))
+
+
 MUTANTS = {
     "base3_msd_first": lambda mp: mp.setattr(o, "POW3", o.POW3[::-1].copy()),
     "base3_pad_first": lambda mp: mp.setattr(o, *_wrap("pack_base3", _pack3_pad_first)),
@@ -88,6 +120,16 @@ MUTANTS = {
     "scale_group_64": lambda mp: mp.setattr(o, *_wrap("dequantize", _dequant_group64)),
     "scale_dropped": lambda mp: mp.setattr(o, *_wrap("dequantize", _dequant_no_scale)),
     "gemv_outputs_reversed": lambda mp: mp.setattr(o, *_wrap("gemv", _gemv_transposed)),
+    "rel_err_mean_for_max": lambda mp: mp.setattr(
+        o, *_wrap("rel_err", _rel_err_variant(mean=True))),
+    "rel_err_global_rms": lambda mp: mp.setattr(
+        o, *_wrap("rel_err", _rel_err_variant(global_rms=True))),
+    "rel_err_candidate_denominator": lambda mp: mp.setattr(
+        o, *_wrap("rel_err", _rel_err_variant(cand_den=True))),
+    "rel_err_floor_dropped": lambda mp: mp.setattr(
+        o, *_wrap("rel_err", _rel_err_variant(no_floor=True))),
+    "normwise_per_row": lambda mp: mp.setattr(o, *_wrap("normwise_err", _normwise_per_row_max)),
+    "normwise_not_divided": lambda mp: mp.setattr(o, *_wrap("normwise_err", _normwise_no_division)),
 }
 
 
