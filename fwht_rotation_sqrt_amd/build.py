@@ -28,7 +28,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}"
 # live across its K loop; in the accumulation-register form the compiler
 # copies them between registers around every matrix instruction, in the
 # VGPR form it updates them in place.
-FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              # the batch-1 decode kernel's arguments arrive in SGPRs at wave launch instead of
+              # through a scalar load of the argument segment, which waits behind the weight stream
+              "decode1.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _hipcc() -> str:

@@ -99,6 +99,10 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
                          static_cast<hipStream_t>(stream));
     return finish_launch();
   }
+  if (tb::decode1_supports(packing, int(B), int(N), int(K)) &&
+      tb::launch_decode1(packed, scales, xr, xr_dtype, nullptr, false, y, int(N), int(K),
+                         static_cast<hipStream_t>(stream)))
+    return finish_launch();
   const size_t xsz = xr_dtype == TB_F32 ? 4 : 2;
   for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
     const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;
@@ -118,6 +122,10 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
   if (!packed || !scales || !x || !sign_bits || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y))
     return TB_ERR_ALIGN;
+  if (tb::decode1_supports(packing, int(B), int(N), int(K)) &&
+      tb::launch_decode1(packed, scales, x, x_dtype, sign_bits, true, y, int(N), int(K),
+                         static_cast<hipStream_t>(stream)))
+    return finish_launch();
   const size_t xsz = x_dtype == TB_F32 ? 4 : 2;
   for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
     const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;

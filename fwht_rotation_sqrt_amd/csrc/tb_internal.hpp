@@ -31,6 +31,11 @@ void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, con
                  int m, int n, int k, hipStream_t s);
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);
+// Batch-1 base-3 decode product on independent matrix-core lane groups (decode1.hip): whether it
+// takes the shape, and the launch (x is x' when rotate is false, else the unrotated x).
+bool decode1_supports(int packing, int b, int n, int k);
+bool launch_decode1(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
+                    const uint32_t* sign_bits, bool rotate, float* y, int n, int k, hipStream_t s);
 
 // Walsh-Hadamard butterflies across lane bits 4 and 5 of a wave (partner
 // lane l ^ 16, then l ^ 32), for 16 values per lane: the lane whose bit is 0

@@ -58,7 +58,12 @@ typedef enum { TB_F32 = 0, TB_F16 = 1, TB_BF16 = 2 } tb_dtype;
 
 /* Bytes of one packed row of K weights: K/4 for 2-bit codes, 26*K/128 for
  * base-3 codes; -1 if K is negative or not a multiple of 128 or the packing
- * code is unknown.  Pure host function. */
+ * code is unknown.  Pure host function.
+ * Pages: "TensorSharp view of Ternary Bonsai 2 27B" (2kiu.com/news/5337570/),
+ * section 1.2 (bits per weight = stored bytes * 8 / weights): with the fp16
+ * scale of each 128-group this gives 2.125 bits/weight for 2-bit codes and
+ * 1.75 for base-3 codes; "Bonsai low-bit learning path", section "Understand
+ * 1.6 bit with five numbers" (five trits per base-3 byte). */
 int64_t tb_packed_row_bytes(int packing, int64_t K);
 
 /* 2-bit packing.  trits: int8 [N][K] with values in {-1,0,1}.  packed: uint8
@@ -81,7 +86,10 @@ int tb_pack_2bit(const int8_t* trits, int64_t N, int64_t K, uint8_t* packed,
 int tb_pack_base3(const int8_t* trits, int64_t N, int64_t K, uint8_t* packed,
                   int32_t* bad_count, void* stream);
 
-/* Inverse of the two packings (the validator of packed weights).  trits: int8
+/* Inverse of the two packings (the validator of packed weights).
+ * Pages: "Bonsai low-bit learning path", section "Understand 1.6 bit with
+ * five numbers": trit i of a base-3 byte b is (b / 3**i) mod 3 - 1 (integer
+ * division), i = 0..4; 2-bit codes decode as t = c - 1.  trits: int8
  * [N][K] out.  bad_count (NULLABLE): +1 per 2-bit code 11 (decoded 0), per
  * base-3 byte >= 243 (its five trits decoded 0) and per group whose last byte
  * has pad digits other than 1.  The products do not check codes: their result
@@ -92,7 +100,7 @@ int tb_unpack(int packing, const uint8_t* packed, int64_t N, int64_t K, int8_t* 
 /* Blockwise rotation xr = R_K x, R_K = blockdiag(H_1024 S_b / 32).
  * Pages: "Ternary Bonsai 2 27B release", section "How the ternary weights
  * reach 1.76 bit" (R = H_n S / sqrt(n), n = 1024, applied blockwise to the
- * activations) and section "Known shortcomings" (this transform is the largest
+ * activations) and section "Known weaknesses" (this transform is the largest
  * cost after the product at batch 1); "TensorSharp view of Ternary Bonsai 2
  * 27B" (2kiu.com/news/5337570/), sections 3.2 and 5.2 (Sylvester-ordered H,
  * butterfly evaluation).
