@@ -12,4 +12,5 @@ from .ternary import (  # noqa: F401
     GROUP, BLOCK, B3_BYTES_PER_GROUP,
     pack_2bit, unpack_2bit, pack_base3, unpack_base3, packed_row_bytes, bits_per_weight,
     hadamard, sign_vector, rotate, dequantize, gemv, gemm, rel_err, normwise_err,
+    TERNARY_CANDIDATES, rotate_weights, f64_to_f16_bits, ternarize, quantize_weights,
 )

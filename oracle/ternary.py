@@ -11,6 +11,10 @@ Pages cited (title, address, section):
        and recovered as (byte // 3**i) % 3 - 1.
   [P4] "TensorSharp view of Ternary Bonsai 2 27B" (2kiu.com/news/5337570/):
        section 1.2 (bits per weight = stored bytes * 8 / parameters),
+       section 2.1 (blockwise ternarisation: each block has its own scale, taken
+       from the mean absolute weight times a correction; w/scale >= thr -> +1,
+       <= -thr -> -1, otherwise 0; the finer form tries a set of candidate
+       thresholds and keeps the one with the least reconstruction error),
        section 3.1 (H is a +-1 matrix with H H^T = n I),
        section 3.2 (Sylvester construction, printed H_4),
        section 5.2 (butterfly fast Hadamard divided by sqrt(n)).
@@ -18,7 +22,8 @@ Pages cited (title, address, section):
        "How the ternary weights reach 1.76 bit": ternary weights with one fp16
        scale per 128 weights (g128); the fixed rotated basis
        R = (1/sqrt(n)) H_n S with n = 1024 and S a fixed +-1 diagonal, applied
-       blockwise, and inference computes f(x) = W(Rx).
+       blockwise, and inference computes f(x) = W(Rx); the weights are moved into
+       that basis before they are ternarised.
 
 Readings where the pages leave a step open (each is listed with its reason in
 the design notes of the repository):
@@ -34,6 +39,19 @@ the design notes of the repository):
     which is the recursion of [P4] section 3.2.
   * R: S first, then H, then 1/sqrt(1024) = 1/32; blocks are consecutive
     1024-slices of K; the sign diagonal is a K-bit mask (bit set = -1).
+  * weights into the basis: W' = W R_K^T, so that W x = W' (R_K x) exactly;
+    each row w of W becomes R_K w, the same transform as an activation row.
+  * ternariser, per 128-group of W' (the scale groups): with a = mean |w|, the
+    candidate thresholds are c_j a, c_j = (j + 1) / 32 for j = 0..63; candidate
+    j keeps the weights with |w| >= c_j a as sign(w) and zeroes the rest; its
+    scale is the least-squares scale of those trits (the mean kept magnitude,
+    i.e. a times a correction factor) rounded to fp16 (nearest even); its error
+    is the group's squared reconstruction error with that rounded scale
+    (infinite when the scale overflows fp16).  The least error wins, the
+    lowest j on ties.  An all-zero group gives zero trits
+    and scale 0; a group holding a non-finite value, or whose chosen scale
+    overflows fp16, is counted bad and stored as zero trits with scale 0.
+    Every step runs in float64.
 """
 from __future__ import annotations
 
@@ -184,6 +202,77 @@ def gemv(packing: str, packed: np.ndarray, scales_bits: np.ndarray, xr: np.ndarr
 def gemm(packing: str, packed: np.ndarray, scales_bits: np.ndarray, xr: np.ndarray, k: int) -> np.ndarray:
     """Prefill product Y[m][n] = sum_k X'[m][k] W_hat[n][k]; same definition as gemv."""
     return gemv(packing, packed, scales_bits, xr, k)
+
+
+# ---------------------------------------------------------------- ternariser
+
+TERNARY_CANDIDATES = 64     # thresholds (j + 1) / 32 * mean|w|, j = 0..63
+
+
+def rotate_weights(w: np.ndarray, sign_bits: np.ndarray) -> np.ndarray:
+    """W' = W R_K^T in float64, so that W x = W' (R_K x)  [P5].
+
+    Row n of W' is R_K applied to row n of W, i.e. ``rotate`` on the rows.
+    """
+    return rotate(np.asarray(w, dtype=np.float64), sign_bits)
+
+
+def f64_to_f16_bits(v) -> np.ndarray:
+    """float64 -> nearest fp16 (ties to even), one rounding; uint16 bit patterns."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def ternarize(wr: np.ndarray):
+    """Rotated weights [N][K] -> (int8 trits [N][K], uint16 fp16 scale bits [N][K/128],
+    chosen candidate [N][K/128] (-1 for zero or bad groups), bad group count)  [P4 section 2.1].
+
+    Each 128-group is searched over the candidate thresholds independently; see
+    the module notes for the reading of the scale, threshold and error.
+    """
+    wr = np.asarray(wr, dtype=np.float64)
+    n, k = wr.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    with np.errstate(over="ignore", invalid="ignore"):
+        return _ternarize_groups(wr, n, k)
+
+
+def _ternarize_groups(wr, n, k):
+    g = wr.reshape(n * (k // GROUP), GROUP)
+    mag = np.abs(g)
+    finite = np.all(np.isfinite(g), axis=1)
+    a = np.sum(np.where(finite[:, None], mag, 0.0), axis=1) / GROUP       # mean |w|
+    best_err = np.full(len(g), np.inf)
+    best_j = np.zeros(len(g), dtype=np.int64)
+    best_s16 = np.zeros(len(g), dtype=np.uint16)
+    for j in range(TERNARY_CANDIDATES):
+        theta = (j + 1) / 32 * a
+        keep = mag >= theta[:, None]
+        nnz = np.sum(keep, axis=1)
+        kept_sum = np.sum(np.where(keep, mag, 0.0), axis=1)
+        s = np.divide(kept_sum, nnz, out=np.zeros(len(g)), where=nnz > 0)
+        s16_bits = f64_to_f16_bits(s)
+        s16 = s16_bits.view(np.float16).astype(np.float64)
+        err = np.sum(np.where(keep, (mag - s16[:, None]) ** 2, mag * mag), axis=1)
+        better = (err < best_err) | (j == 0)
+        best_err = np.where(better, err, best_err)
+        best_j = np.where(better, j, best_j)
+        best_s16 = np.where(better, s16_bits, best_s16)
+    theta = (best_j + 1) / 32 * a
+    trits = np.where(mag >= theta[:, None], np.sign(g), 0.0).astype(np.int8)
+    bad = ~finite | ~np.isfinite(best_s16.view(np.float16))
+    zero = (a == 0) | bad
+    trits[zero] = 0
+    best_s16 = np.where(zero, 0, best_s16).astype(np.uint16)
+    best_j = np.where(zero, -1, best_j)
+    return (trits.reshape(n, k), best_s16.reshape(n, k // GROUP), best_j.reshape(n, k // GROUP),
+            int(np.sum(bad)))
+
+
+def quantize_weights(w: np.ndarray, sign_bits: np.ndarray):
+    """fp weights W [N][K] (y = W x) -> ternarize(W R_K^T): the offline step that
+    puts W into the rotated basis and onto the g128 ternary grid  [P5], [P4 section 2.1]."""
+    return ternarize(rotate_weights(w, sign_bits))
 
 
 # ---------------------------------------------------------------- error metric

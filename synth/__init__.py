@@ -18,7 +18,9 @@ stand-in shapes and statistics are synthetic):
   * activations: N(0, 1) in fp64, optionally with round(0.001 K) outlier
     channels (the same channels in every row) multiplied by 20, then rounded
     to float32 and, for bf16 inputs, to bf16 (round to nearest even);
-  * sign diagonal: 1024 fair bits (set = -1), tiled over every 1024-block of K.
+  * sign diagonal: 1024 fair bits (set = -1), tiled over every 1024-block of K;
+  * full-precision weights (for the ternariser): N(0, 0.02^2), optionally with
+    outlier input columns multiplied by 20, rounded once to float32.
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ BLOCK = 1024       # rotation block size n
 KEY_BASE = 0x7B500000
 
 # tensor ids inside a workload key
-T_TRITS, T_SCALES, T_X, T_SIGNS, T_OUTLIERS = 0, 1, 2, 3, 4
+T_TRITS, T_SCALES, T_X, T_SIGNS, T_OUTLIERS, T_FP_WEIGHTS = 0, 1, 2, 3, 4, 5
 
 
 def rng(workload: int, tensor: int, layer: int = 0, linear: int = 0) -> np.random.Generator:
@@ -91,6 +93,16 @@ def activations(g: np.random.Generator, rows: int, k: int, outliers: np.ndarray 
     if dtype == "f32":
         return x32
     raise ValueError(dtype)
+
+
+def fp_weights(g: np.random.Generator, n: int, k: int, std: float = 0.02,
+               outliers: np.ndarray | None = None, gain: float = 20.0) -> np.ndarray:
+    """float32 [n][k] full-precision weights (y = W x): N(0, std^2), with the given
+    input columns multiplied by ``gain`` before the single rounding to float32."""
+    w = g.standard_normal((n, k)) * std
+    if outliers is not None and len(outliers):
+        w[:, outliers] *= gain
+    return w.astype(np.float32)
 
 
 def sign_bits(g: np.random.Generator, k: int) -> np.ndarray:

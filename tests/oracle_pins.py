@@ -399,6 +399,173 @@ def pin_normwise_err_hand_cases(o, read_golden=None):
     assert not (o.normwise_err(y, np.ones(2)) < 1e30)
 
 
+# ------------------------------------------------------------------ ternariser
+#
+# The offline step: W' = W R_K^T, then per 128-group a threshold search over
+# c_j mean|w|, c_j = (j + 1) / 32, with the least-squares scale of each
+# candidate's trits rounded to fp16 and the least reconstruction error winning.
+
+def pin_f16_rounding_is_single(o, read_golden=None):
+    """The scale is rounded once, float64 -> fp16, to nearest even (no stop at fp32)."""
+    cases = [
+        (1.0 + 2.0 ** -11 + 2.0 ** -40, 1.0 + 2.0 ** -10),  # above the tie: up (via fp32: 1.0)
+        (1.0 + 2.0 ** -11, 1.0),                           # tie: to even
+        (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),           # tie: to even, up
+        (65519.99, 65504.0), (65520.0, np.inf),            # the top of the range
+        (2.0 ** -25, 0.0), (2.0 ** -25 + 2.0 ** -45, 2.0 ** -24),  # subnormal tie / just above
+        (3 * 2.0 ** -25, 2.0 ** -23), (0.0, 0.0),
+    ]
+    for v, want in cases:
+        got = o.f64_to_f16_bits(np.array([v])).view(np.float16).astype(np.float64)[0]
+        assert got == want, (v, got, want)
+
+
+def _one_group(o, w):
+    t, s, j, bad = o.ternarize(np.asarray(w, dtype=np.float64).reshape(1, 128))
+    return t[0], float(s.view(np.float16).astype(np.float64)[0, 0]), int(j[0, 0]), bad
+
+
+def pin_ternarize_hand_blocks(o, read_golden=None):
+    signs = np.where(np.arange(128) % 3 == 0, -1.0, 1.0)
+    # equal magnitudes: every threshold up to 0.5 keeps all, error 0 -> the first candidate
+    t, s, j, bad = _one_group(o, 0.5 * signs)
+    assert (t == signs).all() and s == 0.5 and j == 0 and bad == 0
+    # 16 weights of 1 among 112 of 0.01: a = (16 + 1.12) / 128 = 0.13375; the first
+    # threshold above 0.01 is 3/32 a = 0.01254 (j = 2), which keeps exactly the 16
+    w = np.full(128, 0.01)
+    w[::8] = 1.0
+    t, s, j, bad = _one_group(o, w * signs)
+    assert j == 2 and s == 1.0 and bad == 0
+    assert (t == np.where(w == 1.0, signs, 0)).all()
+    # all zero: zero trits, scale 0, not bad
+    t, s, j, bad = _one_group(o, np.zeros(128))
+    assert (t == 0).all() and s == 0.0 and j == -1 and bad == 0
+    # non-finite weight, or a scale beyond fp16: bad, stored as zeros
+    for v in (np.nan, np.inf):
+        w = np.full(128, 0.5)
+        w[7] = v
+        t, s, j, bad = _one_group(o, w)
+        assert (t == 0).all() and s == 0.0 and bad == 1
+    # a candidate whose scale overflows fp16 has infinite error: for equal weights of 1e6
+    # only the thresholds above them (c_j > 1, nothing kept, scale 0) are finite
+    t, s, j, bad = _one_group(o, np.full(128, 1e6))
+    assert (t == 0).all() and s == 0.0 and j == 32 and bad == 0
+    # one weight of 1e6 is kept by every threshold (2 a < 1e6), so every candidate overflows
+    w = np.zeros(128)
+    w[3] = 1e6
+    t, s, j, bad = _one_group(o, w)
+    assert (t == 0).all() and s == 0.0 and bad == 1
+    # 65504 is the largest finite fp16: kept
+    t, s, j, bad = _one_group(o, np.full(128, 65504.0))
+    assert (t == 1).all() and s == 65504.0 and bad == 0
+
+
+def _ternarize_by_sorting(w):
+    """Independent search: sort the magnitudes, count each threshold's keepers by
+    bisection, and take the error from prefix sums, E = sum w^2 - 2 s P + n s^2."""
+    import math
+    m = np.abs(w)
+    desc = np.sort(m)[::-1]
+    prefix = np.concatenate([[0.0], np.cumsum(desc)])
+    total = math.fsum(m * m)
+    a = math.fsum(m) / 128
+    best = None
+    for j in range(64):
+        theta = (j + 1) / 32 * a
+        cnt = int(np.searchsorted(-desc, -theta, side="right"))   # magnitudes >= theta
+        s = prefix[cnt] / cnt if cnt else 0.0
+        s16 = float(np.float16(s))
+        e = total - 2 * s16 * prefix[cnt] + cnt * s16 * s16
+        if best is None or e < best[0] - 1e-12 * total:
+            best = (e, j, s16, theta)
+    e, j, s16, theta = best
+    return np.where(m >= theta, np.sign(w), 0).astype(np.int8), s16, j
+
+
+def pin_ternarize_matches_sorted_search(o, read_golden=None):
+    g = np.random.default_rng(20)
+    groups = [g.standard_normal(128), g.laplace(size=128) * 1e-3, g.standard_t(3, size=128),
+              np.abs(g.standard_normal(128)), g.standard_normal(128) * 2.0 ** 12]
+    # dyadic magnitudes k/64 with sum 64, so a = 1/2 and every threshold (j+1)/64 equals
+    # some magnitude: the >= of the threshold rule decides every candidate
+    k = np.full(128, 32)
+    d = g.integers(-31, 32, size=64)
+    k[:64] += d
+    k[64:] -= d
+    groups.append(k / 64 * np.where(g.integers(0, 2, 128) == 1, -1.0, 1.0))
+    sparse = np.zeros(128)
+    sparse[g.choice(128, 5, replace=False)] = g.standard_normal(5)
+    groups.append(sparse)
+    for w in groups:
+        t, s, j, bad = _one_group(o, w)
+        t2, s2, j2 = _ternarize_by_sorting(w)
+        assert bad == 0 and j == j2 and s == s2 and (t == t2).all(), (j, j2, s, s2)
+
+
+def pin_ternarize_invariances(o, read_golden=None):
+    g = np.random.default_rng(21)
+    w = g.standard_normal((6, 256))
+    t, s, j, _ = o.ternarize(w)
+    for p2 in (2.0 ** 5, 2.0 ** -5):           # a power of two moves the scale, not the trits
+        t2, s2, j2, _ = o.ternarize(w * p2)
+        assert (t2 == t).all() and (j2 == j).all()
+        assert (s2.view(np.float16).astype(float) == s.view(np.float16).astype(float) * p2).all()
+    t2, s2, j2, _ = o.ternarize(-w)             # negation flips the trits only
+    assert (t2 == -t).all() and (s2 == s).all()
+    perm = np.concatenate([g.permutation(128), 128 + g.permutation(128)])
+    t2, s2, _, _ = o.ternarize(w[:, perm])      # a permutation inside each group permutes the trits
+    assert (t2 == t[:, perm]).all() and (s2 == s).all()
+
+
+def pin_ternarize_gaussian_distortion(o, read_golden=None):
+    """The best three-level quantiser of N(0, 1) (Max, 1960) has thresholds +-0.612,
+    levels +-1.224 and mean squared error 0.1902; a per-group fitted search can only
+    come in at or just under it, with thresholds near 0.612 sigma."""
+    g = np.random.default_rng(22)
+    w = g.standard_normal((64, 2048))
+    t, s, j, bad = o.ternarize(w)
+    what = t * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    mse = np.mean((what - w) ** 2)
+    assert bad == 0 and 0.175 < mse < 0.1902, mse
+    a = np.mean(np.abs(w).reshape(-1, 128), axis=1)
+    thr = (j.ravel() + 1) / 32 * a
+    assert 0.55 < np.median(thr) < 0.67, np.median(thr)
+    lv = s.view(np.float16).astype(np.float64)
+    assert 1.15 < np.median(lv) < 1.30, np.median(lv)
+
+
+def pin_rotate_weights_identity(o, read_golden=None):
+    """W x = (W R_K^T)(R_K x) for every x: the rotated weights act on rotated inputs."""
+    g = np.random.default_rng(23)
+    sb = g.integers(0, 2 ** 32, size=64, dtype=np.uint64).astype(np.uint32)
+    w = g.standard_normal((12, 2048))
+    x = g.standard_normal((3, 2048))
+    lhs = o.rotate_weights(w, sb) @ o.rotate(x, sb).T
+    assert np.max(np.abs(lhs - w @ x.T)) < 1e-10
+
+
+def pin_quantize_tracks_fp_product(o, read_golden=None):
+    """y = W_hat (R x) against W x: Gaussian weights give the quantiser's own error
+    (sqrt 0.187); weights with 1 % outlier columns x20 stay there in the rotated basis,
+    and ternarising them unrotated is more than twice as bad in squared error."""
+    g = np.random.default_rng(24)
+    sb = g.integers(0, 2 ** 32, size=64, dtype=np.uint64).astype(np.uint32)
+    w = g.standard_normal((64, 2048))
+    cols = g.choice(2048, 20, replace=False)
+    w_out = w.copy()
+    w_out[:, cols] *= 20.0
+    x = g.standard_normal((32, 2048))
+    for ww, lo, hi in ((w, 0.40, 0.46), (w_out, 0.38, 0.46)):
+        t, s, _, bad = o.quantize_weights(ww, sb)
+        what = t * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+        e = o.normwise_err(o.rotate(x, sb) @ what.T, x @ ww.T)
+        assert bad == 0 and lo < e < hi, e
+    t, s, _, _ = o.ternarize(w_out)
+    what = t * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    e_unrot = o.normwise_err(x @ what.T, x @ w_out.T)
+    assert e_unrot ** 2 > 2 * 0.46 ** 2, e_unrot
+
+
 ALL_PINS = [
     pin_base3_page_example, pin_base3_bijection, pin_base3_pad_and_size, pin_base3_bad_counts,
     pin_2bit_base4_number, pin_2bit_bijection, pin_2bit_bad_counts, pin_bits_per_weight,
@@ -407,4 +574,7 @@ ALL_PINS = [
     pin_gemv_bruteforce, pin_gemv_associativity, pin_gemv_unit_inputs,
     pin_gemv_zero_and_linearity, pin_gemm_rows_are_gemv,
     pin_rel_err_hand_cases, pin_normwise_err_hand_cases,
+    pin_f16_rounding_is_single, pin_ternarize_hand_blocks, pin_ternarize_matches_sorted_search,
+    pin_ternarize_invariances, pin_ternarize_gaussian_distortion, pin_rotate_weights_identity,
+    pin_quantize_tracks_fp_product,
 ]

@@ -106,7 +106,82 @@ def _normwise_no_division(orig, y, yref):
     return float(np.linalg.norm(np.asarray(y, float) - np.asarray(yref, float)))
 
 
+def _ternarize_variant(strict=False, mean_all=False, grid_from_zero=False, kept_error_only=False,
+                       sign_flip=False, unrounded_error=False, last_on_ties=False):
+    """The oracle's threshold search with one planted slip."""
+    def fn(orig, wr):
+        wr = np.asarray(wr, dtype=np.float64)
+        n, k = wr.shape
+        g = wr.reshape(-1, 128)
+        mag = np.abs(g)
+        finite = np.all(np.isfinite(g), axis=1)
+        a = np.sum(np.where(finite[:, None], mag, 0.0), axis=1) / 128
+        best = np.full(len(g), np.inf)
+        bj = np.zeros(len(g), dtype=np.int64)
+        bs = np.zeros(len(g), dtype=np.uint16)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for j in range(64):
+                c = j / 32 if grid_from_zero else (j + 1) / 32
+                keep = mag > (c * a)[:, None] if strict else mag >= (c * a)[:, None]
+                nnz = keep.sum(1)
+                if mean_all:
+                    s = a.copy()
+                else:
+                    s = np.divide(np.where(keep, mag, 0).sum(1), nnz, out=np.zeros(len(g)), where=nnz > 0)
+                sb = o.f64_to_f16_bits(s)
+                s16 = s if unrounded_error else sb.view(np.float16).astype(np.float64)
+                kept = np.where(keep, (mag - s16[:, None]) ** 2, 0.0)
+                err = (kept if kept_error_only else kept + np.where(keep, 0.0, mag * mag)).sum(1)
+                better = (err <= best) if last_on_ties else (err < best)
+                better |= j == 0
+                best = np.where(better, err, best)
+                bj = np.where(better, j, bj)
+                bs = np.where(better, sb, bs)
+            c = bj / 32 if grid_from_zero else (bj + 1) / 32
+            keep = mag > (c * a)[:, None] if strict else mag >= (c * a)[:, None]
+            t = np.where(keep, np.sign(g), 0.0).astype(np.int8)
+            if sign_flip:
+                t = -t
+            bad = ~finite | ~np.isfinite(bs.view(np.float16))
+            zero = (a == 0) | bad
+            t[zero] = 0
+            bs = np.where(zero, 0, bs).astype(np.uint16)
+            bj = np.where(zero, -1, bj)
+        return t.reshape(n, k), bs.reshape(n, k // 128), bj.reshape(n, k // 128), int(bad.sum())
+    return fn
+
+
+def _rotate_weights_untransposed(orig, w, sb):
+    """W R_K instead of W R_K^T: each row times H S / 32 as a row vector."""
+    w = np.asarray(w, dtype=float)
+    k = w.shape[1]
+    plus = np.zeros(k // 32, dtype=np.uint32)
+    return o.rotate(w, plus) * o.sign_vector(sb, k)
+
+
 MUTANTS = {
+    "ternarize_strict_threshold": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(strict=True))),
+    "ternarize_scale_mean_of_all": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(mean_all=True))),
+    "ternarize_grid_from_zero": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(grid_from_zero=True))),
+    "ternarize_error_kept_only": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(kept_error_only=True))),
+    "ternarize_sign_flipped": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(sign_flip=True))),
+    "ternarize_last_on_ties": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(last_on_ties=True))),
+    "ternarize_unrounded_error": lambda mp: mp.setattr(
+        o, *_wrap("ternarize", _ternarize_variant(unrounded_error=True))),
+    "f16_via_f32": lambda mp: mp.setattr(
+        o, *_wrap("f64_to_f16_bits", lambda orig, v: np.asarray(v, dtype=np.float64)
+                  .astype(np.float32).astype(np.float16).view(np.uint16))),
+    "rotate_weights_untransposed": lambda mp: mp.setattr(
+        o, *_wrap("rotate_weights", _rotate_weights_untransposed)),
+    "quantize_skips_rotation": lambda mp: mp.setattr(
+        o, *_wrap("quantize_weights", lambda orig, w, sb: o.ternarize(w))),
+
     "base3_msd_first": lambda mp: mp.setattr(o, "POW3", o.POW3[::-1].copy()),
     "base3_pad_first": lambda mp: mp.setattr(o, *_wrap("pack_base3", _pack3_pad_first)),
     "2bit_msb_first": lambda mp: mp.setattr(o, *_wrap("pack_2bit", _pack2_msb_first)),
