@@ -23,7 +23,7 @@ TB_GEMV_KERNEL_BATCH = 8  # tb_linear above this: chunks of 8 rows, each re-stre
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",
-           "tb_gemv", "tb_linear", "tb_gemm", "tb_status_string", "tb_last_hip_error")
+           "tb_gemv", "tb_linear", "tb_gemm", "tb_ternarize", "tb_status_string", "tb_last_hip_error")
 
 _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGNATURES = {
@@ -35,6 +35,7 @@ _SIGNATURES = {
     "tb_gemv": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _I64, _I64, _I64, _VP]),
     "tb_linear": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_gemm": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
+    "tb_ternarize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "tb_status_string": (ctypes.c_char_p, [_INT]),
     "tb_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -245,3 +246,27 @@ def tb_gemm(packing, packed, scales, xr, y=None, stream=None):
     _call("tb_gemm", _packing(packing), _ptr(packed), _ptr(scales), _ptr(xr), _ptr(y), m, n, k,
           _stream(stream))
     return y
+
+
+def tb_ternarize(w, sign_bits=None, trits=None, scales=None, bad_count=None, stream=None):
+    """fp32 weights W[N][K] -> (int8 trits [N][K], fp16 scales [N][K/128]) of W R_K^T
+    (sign_bits=None: W is already in the rotated basis, the search alone)."""
+    _check(w, "w", (torch.float32,))
+    _rank2(w, "w")
+    n, k = w.shape
+    if k % 1024:
+        raise ValueError(f"K = {k} is not a multiple of 1024")
+    if sign_bits is not None:
+        _signs(sign_bits, k)
+    if trits is None:
+        trits = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 128), dtype=torch.float16, device=w.device)
+    _check(trits, "trits", (torch.int8,))
+    _shape(trits, "trits", (n, k))
+    _check(scales, "scales", (torch.float16,))
+    _shape(scales, "scales", (n, k // 128))
+    _count(bad_count)
+    _call("tb_ternarize", _ptr(w), n, k, _ptr(sign_bits), _ptr(trits), _ptr(scales), _ptr(bad_count),
+          _stream(stream))
+    return trits, scales

@@ -158,6 +158,16 @@ int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const ui
   return finish_launch();
 }
 
+int tb_ternarize(const float* w, int64_t N, int64_t K, const uint32_t* sign_bits, int8_t* trits,
+                 uint16_t* scales, int32_t* bad_count, void* stream) {
+  if (N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(N, K)) return TB_ERR_SHAPE;
+  if (N == 0) return TB_OK;
+  if (!w || !trits || !scales) return TB_ERR_NULL;
+  if (!aligned16(w) || !aligned16(scales) || (sign_bits && !aligned16(sign_bits))) return TB_ERR_ALIGN;
+  tb::launch_ternarize(w, N, K, sign_bits, trits, scales, bad_count, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 const char* tb_status_string(int status) {
   switch (status) {
     case TB_OK: return "ok";

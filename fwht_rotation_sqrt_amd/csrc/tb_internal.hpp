@@ -31,6 +31,8 @@ void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, con
                  int m, int n, int k, hipStream_t s);
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);
+void launch_ternarize(const float* w, int64_t n, int64_t k, const uint32_t* sign_bits, int8_t* trits,
+                      uint16_t* scales, int32_t* bad_count, hipStream_t s);
 // Batch-1 base-3 decode product on independent matrix-core lane groups (decode1.hip): whether it
 // takes the shape, and the launch (x is x' when rotate is false, else the unrotated x).
 bool decode1_supports(int packing, int b, int n, int k);

@@ -160,6 +160,32 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Offline quantiser: fp32 weights W (y = W x) -> ternary trits and g128 fp16
+ * scales of W' = W R_K^T, the weights in the rotated basis, so that
+ * W x is approximated by (trits * scales)(R_K x).
+ * Pages: "Ternary Bonsai 2 27B release", section "How the ternary weights
+ * reach 1.76 bit" (the weights are moved into the fixed rotated basis before
+ * they are ternarised; one fp16 scale per 128 weights); "TensorSharp view of
+ * Ternary Bonsai 2 27B" (2kiu.com/news/5337570/), section 2.1 (a scale per
+ * block from its mean absolute weight times a correction; |w / scale| below
+ * the threshold gives 0, otherwise the sign; the finer form tries candidate
+ * thresholds and keeps the least reconstruction error).
+ * Per 128-group of W' with a = mean |w|: candidate j = 0..63 keeps the
+ * weights with |w| >= (j + 1) / 32 * a as sign(w) and zeroes the rest; its
+ * scale is the mean kept magnitude rounded once to fp16 (nearest even); the
+ * candidate with the least squared reconstruction error under that rounded
+ * scale wins (the lowest j on ties; a scale that overflows fp16 counts as
+ * infinite error).  Rotation and search run in fp64.
+ * w: fp32 [N][K].  sign_bits: uint32 [K/32] as for tb_fwht_rotate, or NULL
+ * when w is already in the rotated basis (the search alone).  trits: int8
+ * [N][K] out; scales: fp16 [N][K/128] out; pack the trits afterwards with
+ * tb_pack_2bit or tb_pack_base3.  bad_count (NULLABLE): +1 per group holding
+ * a non-finite value or whose chosen scale overflows fp16; such groups, and
+ * all-zero groups, are written as zero trits with scale 0.  K % 1024 == 0;
+ * w, scales (and sign_bits when given) 16-byte aligned. */
+int tb_ternarize(const float* w, int64_t N, int64_t K, const uint32_t* sign_bits, int8_t* trits,
+                 uint16_t* scales, int32_t* bad_count, void* stream);
+
 /* Static text for a status code. */
 const char* tb_status_string(int status);
 

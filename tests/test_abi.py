@@ -129,6 +129,23 @@ def test_gemm_validation():
     assert g(0, P, P, P, P, 0, 8, 128, None) == OK
 
 
+def test_ternarize_validation():
+    lib = tb.library()
+    g = lib.tb_ternarize
+    # (w, N, K, sign_bits, trits, scales, bad_count, stream)
+    assert g(P, 4, 1152, P, P, P, None, None) == SHAPE             # K % 1024 != 0
+    assert g(P, -1, 1024, P, P, P, None, None) == SHAPE
+    assert g(P, 4, 0, P, P, P, None, None) == SHAPE
+    assert g(P, 1 << 20, 1 << 12, P, P, P, None, None) == SHAPE   # N K beyond 32-bit offsets
+    assert g(None, 4, 1024, P, P, P, None, None) == NULL
+    assert g(P, 4, 1024, P, None, P, None, None) == NULL
+    assert g(P, 4, 1024, P, P, None, None, None) == NULL
+    assert g(MIS, 4, 1024, P, P, P, None, None) == ALIGN
+    assert g(P, 4, 1024, MIS, P, P, None, None) == ALIGN
+    assert g(P, 4, 1024, P, P, MIS, None, None) == ALIGN
+    assert g(None, 0, 1024, None, None, None, None, None) == OK   # empty call
+
+
 def test_status_strings():
     lib = tb.library()
     for st in range(7):
