@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-token", action="store_true", help="skip the 64-layer decode token leg")
+    ap.add_argument("--no-stream", action="store_true", help="skip the read-ceiling leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating HBM byte counters) and exit")
     ap.add_argument("--gemv-batch", type=int, metavar="B",
@@ -65,7 +67,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "tb_gemv_base3_17408x5120_b1_traffic.md")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "tb_linear_base3_17408x5120_b1_traffic.md")
 
 
 def gemv_traffic_bytes():
@@ -171,7 +173,12 @@ def bench_decode(d, steps, warmup):
     t_fused = event_time(g_fused) / steps
     t_gemv = event_time(g_gemv) / steps
     t_rot = event_time(g_rot) / steps
-    return wall, t_fused, t_gemv, t_rot
+    # the shader clock while the product runs: about 3 s of replays queued, rocm-smi read meanwhile
+    for _ in range(max(1, int(3.0 / max(t_fused * steps, 1e-6)))):
+        g_fused.replay()
+    sclk = shader_clock()
+    torch.cuda.synchronize()
+    return wall, t_fused, t_gemv, t_rot, sclk
 
 
 def bench_gemm(steps, packing="2bit"):
@@ -204,31 +211,81 @@ def bench_gemm(steps, packing="2bit"):
                 tokens_per_s=m / (t_gemm + t_rot))
 
 
-def cpu_baseline(d, budget_s=15.0):
-    """The oracle (fp64 numpy) on the same decode workload: rotate + GEMV, whole rows."""
-    import oracle
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = 1
-    li, n, k = d["li"], d["n"], d["k"]
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """The host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(env))) if env and env.isdigit() else n
+
+
+def cpu_baseline(d, budget_s=(8.0, 5.0)):
+    """The plain C++ oracle (fp64 loops) on the same decode step, rotate + product over all
+    17408 rows: single-threaded, then with its output rows split over every host thread."""
+    import oracle
+    from oracle import cpp_oracle
+    li, k = d["li"], d["k"]
     packed, _ = oracle.pack_base3(li.trits)
     x64 = synth.bf16_bits_to_f64(li.x)
-    rows = n
-    t0 = time.perf_counter()
-    done_bytes = 0
-    runs = 0
-    while True:
-        xr = oracle.rotate(x64, li.signs)
-        oracle.gemv("base3", packed[:rows], li.scales[:rows], xr, k)
-        done_bytes += packed[:rows].nbytes + li.scales[:rows].nbytes
-        runs += 1
-        if time.perf_counter() - t0 > budget_s or runs >= 8:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{runs} full passes of rotate+GEMV (17408x5120 base-3, batch 1) in fp64 numpy, {el:.1f} s"}
+    per = packed.nbytes + li.scales.nbytes
+    out = {}
+    for threads, budget in zip((1, host_threads()), budget_s):
+        t0 = time.perf_counter()
+        runs = 0
+        while runs < 1 or time.perf_counter() - t0 < budget:
+            cpp_oracle.linear("base3", packed, li.scales, x64, li.signs, threads)
+            runs += 1
+        el = time.perf_counter() - t0
+        out[threads] = (runs * per / el / 1e9, runs, el)
+    cores = host_threads()
+    v1, r1, e1 = out[1]
+    vn, rn, en = out[cores]
+    return {"value": round(vn, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "single_thread_value": round(v1, 5), "cpu_model": cpu_model(),
+            "sample": f"plain C++ fp64 oracle, rotate + product of the full 17408x5120 base-3 step at batch 1: "
+                      f"{rn} passes in {en:.1f} s on {cores} threads, {r1} passes in {e1:.1f} s on one"}
+
+
+def stream_ceiling(per_copy, reps=20):
+    """The library's read-only stream kernel (tb_stream_read): at the decode step's size, cycling
+    through > 512 MB of buffers like the weights, and once over 2 GB; GB/s from HIP events."""
+    sink = torch.zeros(tb.TB_STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    size = -(-per_copy // 16) * 16
+    copies = max(2, -(-CACHE_BYTES // size))
+    bufs = [torch.ones(size, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    steps = 4 * copies
+
+    def small():
+        for i in range(steps):
+            tb.tb_stream_read(bufs[i % copies], sink, per_copy // 16 * 16)
+
+    _, g = time_graph(small, small)
+    t_small = event_time(g, 3) / steps
+    del g, bufs
+    big_bytes = 2_000_000_000
+    big = torch.ones(big_bytes, dtype=torch.uint8, device="cuda")
+
+    def large():
+        for _ in range(reps // 4):
+            tb.tb_stream_read(big, sink)
+
+    _, g = time_graph(large, large)
+    t_big = event_time(g, 2) / (reps // 4)
+    del g, big
+    return {"kernel": "tb_stream_read (16-byte loads, 8 in flight per lane)",
+            "gbs_at_step_size": round(per_copy // 16 * 16 / t_small / 1e9, 1), "step_size_bytes": per_copy // 16 * 16,
+            "us_at_step_size": round(t_small * 1e6, 3),
+            "gbs_at_2GB": round(big_bytes / t_big / 1e9, 1)}
 
 
 # ---------------------------------------------------------------- --suite
@@ -286,8 +343,15 @@ def suite_linear(packing, n, k, b, gen, steps=50):
         for i in range(steps):
             tb.tb_gemv(packing, ps[i % copies], ss[i % copies], xr, y=y)
 
+    need = tb.tb_linear_workspace_bytes(packing, b, n, k)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def fused_ws():
+        for i in range(steps):
+            tb.tb_linear_ws(packing, ps[i % copies], ss[i % copies], x, sg, workspace=ws, y=y)
+
     out = {}
-    for name, fn in (("fused", fused), ("rotate", rot), ("gemv", gemv)):
+    for name, fn in (("fused", fused), ("rotate", rot), ("gemv", gemv), ("ws", fused_ws)):
         _, g = time_graph(fn, fn)
         out[name] = event_time(g, 3) / steps * 1e6
         del g
@@ -296,7 +360,7 @@ def suite_linear(packing, n, k, b, gen, steps=50):
     return out
 
 
-def suite_token(gen, layers=64, reps=10):
+def suite_token(gen, layers=64, reps=10, per_call=True):
     """One decode token at batch 1 through 64 layers of base-3 linears, q/k/v and
     gate/up concatenated (4 calls per layer): whole-token graph time, fused and
     separate routes, and the rotation's share of the separate route."""
@@ -337,7 +401,7 @@ def suite_token(gen, layers=64, reps=10):
         _, g = time_graph(fn, fn)
         res[name] = event_time(g, reps)
         del g
-    for j, (nm, n, k) in enumerate(shapes):
+    for j, (nm, n, k) in enumerate(shapes if per_call else ()):
         _, g = time_graph(lambda j=j: fused(j), lambda j=j: fused(j))
         res["call_" + nm] = (n, k, event_time(g, reps) / layers)
         del g
@@ -374,7 +438,8 @@ def suite_read_calibration(reps=10):
 
 
 def shader_clock():
-    """The current sclk line of rocm-smi, or a note that it was not available."""
+    """The current sclk line of rocm-smi (the clock while this is called), or a note that it
+    was not available."""
     import subprocess
     try:
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
@@ -403,10 +468,11 @@ def run_suite(path, argv):
     big = []
     gate = synth.BLOCK_LINEARS[4]
     for packing in ("2bit", "base3"):
-        for b in (2, 4, 9, 16, 32):
+        for b in (2, 4, 8, 9, 16, 32):
             r = suite_linear(packing, gate.n, gate.k, b, gen, steps=20)
             big.append((packing, b, r))
-            print(f"gate {packing} b{b}: fused {r['fused']:.2f} us, gemv {r['gemv']:.2f} us", flush=True)
+            print(f"gate {packing} b{b}: fused {r['fused']:.2f} us, ws {r['ws']:.2f} us, gemv {r['gemv']:.2f} us",
+                  flush=True)
     tok = suite_token(gen)
     print(f"token: fused {tok['fused'] * 1e3:.3f} ms, separate {tok['separate'] * 1e3:.3f} ms", flush=True)
     sclk = shader_clock()
@@ -436,14 +502,17 @@ def run_suite(path, argv):
     lines.append("")
     lines.append("## Other batch sizes on gate (17408x5120)")
     lines.append("")
-    lines.append("Above 8 rows, tb_gemv streams the weights once (fp16 matrix cores, gemv_wide.hip); "
-                 "tb_linear runs chunks of 8 rows, each streaming the weights again.")
+    lines.append("From the measured crossover on (here batch 9 for 2-bit, 8 for base-3), tb_gemv streams the "
+                 "weights once (fp16 matrix cores, gemv_wide.hip); tb_linear_ws rotates into the caller's "
+                 "workspace and does the same; tb_linear (no workspace) runs chunks of 8 rows above 8, each "
+                 "streaming the weights again.")
     lines.append("")
-    lines.append("| packing | batch | tb_linear us | tb_gemv us | weight GB/s (tb_linear) | weight GB/s (tb_gemv) |")
-    lines.append("|---|---|---|---|---|---|")
+    lines.append("| packing | batch | tb_linear us | tb_linear_ws us | tb_gemv us | weight GB/s (tb_linear_ws) | "
+                 "weight GB/s (tb_gemv) |")
+    lines.append("|---|---|---|---|---|---|---|")
     for packing, b, r in big:
-        lines.append(f"| {packing} | {b} | {r['fused']:.2f} | {r['gemv']:.2f} | "
-                     f"{r['bytes'] / (r['fused'] * 1e-6) / 1e9:.0f} | {r['bytes'] / (r['gemv'] * 1e-6) / 1e9:.0f} |")
+        lines.append(f"| {packing} | {b} | {r['fused']:.2f} | {r['ws']:.2f} | {r['gemv']:.2f} | "
+                     f"{r['bytes'] / (r['ws'] * 1e-6) / 1e9:.0f} | {r['bytes'] / (r['gemv'] * 1e-6) / 1e9:.0f} |")
     lines.append("")
     lines.append("## Decode token stream: 64 layers, base-3, batch 1 (q/k/v and gate/up concatenated)")
     lines.append("")
@@ -525,7 +594,7 @@ def main():
         print(json.dumps(bench_gemv_batch(args.gemv_batch, args.steps)), flush=True)
         return
     d = decode_setup()
-    wall, t_fused, t_gemv, t_rot = bench_decode(d, args.steps, args.warmup)
+    wall, t_fused, t_gemv, t_rot, sclk = bench_decode(d, args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     per_copy = d["per_copy"]
     value = per_copy / (wall / args.steps) / 1e9
@@ -533,6 +602,13 @@ def main():
     traffic = gemv_traffic_bytes()
     gemm = None if args.no_gemm else bench_gemm(args.steps)
     gemm3 = None if args.no_gemm else bench_gemm(args.steps, "base3")
+    stream = None if args.no_stream else stream_ceiling(per_copy)
+    token = None
+    if not args.no_token:
+        del d["packed"], d["scales"]
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(SUITE_SEED)
+        token = suite_token(gen, reps=3, per_call=False)
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
     rec = {
         "metric": "packed-ternary GEMV HBM GB/s (% peak) + pp512 GEMM TFLOP/s, K=5120",
@@ -545,7 +621,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # batch-1 base-3 product: x' in four fp6 (e2m3) limbs with a power-of-two scale per
+        # 128-group, trits as fp4 (e2m1) codes, fp32 accumulation; the rotation in fp32
+        "dtype": "fp6x4-limb*fp4->f32",
         "data": "synthetic",
         "config": {"workload": "gemv_ffn_17408x5120_base3_b1", "n": d["n"], "k": d["k"], "batch": 1,
                    "packing": "base3", "bits_per_weight": 1.75, "bytes_per_step": per_copy,
@@ -558,7 +636,11 @@ def main():
                      "traffic_bytes_per_launch": traffic,
                      "algorithmic_bytes_per_launch": per_copy,
                      "kernel": "tb_linear base-3 17408x5120 b1 (fused rotation)",
-                     "kernel_us": round(t_fused * 1e6, 3)},
+                     "kernel_us": round(t_fused * 1e6, 3),
+                     "frac_of_measured_ceiling": None if stream is None else
+                     round(fused_gbs / stream["gbs_at_step_size"], 4)},
+        "stream_ceiling": stream,
+        "sclk_during_decode": sclk,
         "separate_route_us": {"tb_fwht_rotate_b1_k5120": round(t_rot * 1e6, 3),
                               "tb_gemv_base3_17408x5120_b1": round(t_gemv * 1e6, 3)},
         "tokens_per_s_equiv_this_linear": round(1.0 / (wall / args.steps), 1),
@@ -572,6 +654,17 @@ def main():
     if gemm3:
         rec["pp512_gemm_base3"] = {"tflops": round(gemm3["tflops"], 2), "us": round(gemm3["us"], 2),
                                    "frac_of_fp16_mfma_peak": round(gemm3["frac"], 4)}
+    if token:
+        t_f, t_r, t_g = token["fused"], token["rotate_only"], token["gemv_only"]
+        rec["decode_token_64_layers"] = {
+            "tokens_per_s_equiv": round(1.0 / t_f, 1), "ms_per_token": round(t_f * 1e3, 4),
+            "weight_bytes_per_token": token["bytes"], "gbs": round(token["bytes"] / t_f / 1e9, 1),
+            "frac_of_hbm_peak": round(token["bytes"] / t_f / 1e9 / HBM_PEAK_GBS, 4),
+            "calls_per_token": token["calls_fused"],
+            "separate_route_ms": round(token["separate"] * 1e3, 4),
+            "fwht_share_of_separate_route": round(t_r / (t_r + t_g), 4),
+            "workload": "64 layers x (qkv 15360x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408), "
+                        "base-3, batch 1, tb_linear per call, one HIP graph"}
     print(json.dumps(rec), flush=True)
 
 

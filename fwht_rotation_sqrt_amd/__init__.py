@@ -20,10 +20,12 @@ TB_PACK_2BIT, TB_PACK_BASE3 = 0, 1
 TB_F32, TB_F16, TB_BF16 = 0, 1, 2
 TB_GEMV_MAX_BATCH = 32   # tb_gemv: one pass over the weights at any batch up to this
 TB_GEMV_KERNEL_BATCH = 8  # tb_linear above this: chunks of 8 rows, each re-streaming the weights
+TB_STREAM_SINK_WORDS = 8192
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",
-           "tb_gemv", "tb_linear", "tb_gemm", "tb_ternarize", "tb_status_string", "tb_last_hip_error")
+           "tb_gemv", "tb_linear", "tb_linear_workspace_bytes", "tb_linear_ws", "tb_gemm", "tb_ternarize",
+           "tb_stream_read", "tb_status_string", "tb_last_hip_error")
 
 _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGNATURES = {
@@ -34,8 +36,11 @@ _SIGNATURES = {
     "tb_fwht_rotate": (_INT, [_VP, _INT, _VP, _INT, _I64, _I64, _VP, _VP]),
     "tb_gemv": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _I64, _I64, _I64, _VP]),
     "tb_linear": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP]),
+    "tb_linear_workspace_bytes": (_I64, [_INT, _I64, _I64, _I64]),
+    "tb_linear_ws": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP]),
     "tb_gemm": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_ternarize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "tb_stream_read": (_INT, [_VP, _I64, _VP, _I64, _VP]),
     "tb_status_string": (ctypes.c_char_p, [_INT]),
     "tb_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -233,6 +238,35 @@ def tb_linear(packing, packed, scales, x, sign_bits, y=None, stream=None):
     return y
 
 
+def tb_linear_workspace_bytes(packing, b: int, n: int, k: int) -> int:
+    return int(library().tb_linear_workspace_bytes(_packing(packing), int(b), int(n), int(k)))
+
+
+def tb_linear_ws(packing, packed, scales, x, sign_bits, workspace=None, y=None, stream=None):
+    """tb_linear with one pass over the weights at every batch; x' goes to ``workspace``
+    (a 16-byte aligned device tensor of at least tb_linear_workspace_bytes bytes)."""
+    _check(x, "x", tuple(_ACT_DT))
+    _rank2(x, "x")
+    b, k = x.shape
+    n = _weights(packing, packed, scales, k)
+    _signs(sign_bits, k)
+    need = tb_linear_workspace_bytes(packing, b, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _check(y, "y", (torch.float32,))
+    _shape(y, "y", (b, n))
+    _call("tb_linear_ws", _packing(packing), _ptr(packed), _ptr(scales), _ptr(x), _ACT_DT[x.dtype],
+          _ptr(sign_bits), _ptr(y), b, n, k, _ptr(workspace), ws_bytes, _stream(stream))
+    return y
+
+
 def tb_gemm(packing, packed, scales, xr, y=None, stream=None):
     """Y[M][N] = X'[M][K] (fp16) times the packed ternary weights, fp32 out."""
     _check(xr, "xr", (torch.float16,))
@@ -270,3 +304,15 @@ def tb_ternarize(w, sign_bits=None, trits=None, scales=None, bad_count=None, str
     _call("tb_ternarize", _ptr(w), n, k, _ptr(sign_bits), _ptr(trits), _ptr(scales), _ptr(bad_count),
           _stream(stream))
     return trits, scales
+
+
+def tb_stream_read(src, sink, nbytes=None, stream=None):
+    """Read the first nbytes (default: all) of a device tensor once; the measured HBM ceiling."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _check(sink, "sink", (torch.int32,))
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if not 0 <= nbytes <= total:
+        raise ValueError(f"nbytes = {nbytes} outside 0..{total}")
+    _call("tb_stream_read", _ptr(src), nbytes, _ptr(sink), sink.numel(), _stream(stream))

@@ -25,10 +25,13 @@
 //     -2^-14 sum_{k in g} x'[b][k], which one chain of matrix instructions
 //     with the constant B operand -2^-14 gives once per group for all tiles.
 //     Then acc += (2^14 s) * partial (2^14 s is exact in fp32).
-//   * fp32 activations are split into hi (x with its mantissa cut to fp16
-//     precision) and lo = fp16(x - hi); both go through the matrix cores into
-//     the same accumulator, so x is carried to about 2^-21 of its size (fp16
-//     range: |x| < 65504; below 2^-14 the error is at most 2^-24 absolute).
+//   * fp32 activations first get a power-of-two scale per (activation row,
+//     group): 2^-e with e chosen so that the group's largest |x'| of the row
+//     lands in [2^14, 2^15).  The scaled values are split into hi (mantissa cut
+//     to fp16 precision) and lo = fp16(x - hi); both go through the matrix
+//     cores into the same accumulator, and the group's partial sum is scaled
+//     back by 2^e in fp32.  So any finite fp32 x' is carried to about 2^-21 of
+//     its size, with an absolute floor near 2^-38 of the group's largest value.
 //     fp16 activations are used as they are.
 //
 // K order inside a group (any order works when both operands use it): lane
@@ -107,17 +110,37 @@ __device__ __forceinline__ void a_issue(ARaw<XF32>& r, __amdgpu_buffer_rsrc_t xr
   for (int i = 0; i < (XF32 ? 8 : 4); ++i) r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u * i, 0, 0);
 }
 
+// The exponent e of the (activation row, group) scale: the largest |x'| of the row's 128 values
+// (this lane's 32 and those of the lanes l ^ 16, l ^ 32, l ^ 48, which hold the row's other
+// quarters) times 2^-e lies in [2^14, 2^15).  All four lanes get the same e; 0 for an all-zero group.
+__device__ __forceinline__ int a_exponent(const ARaw<1>& r) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m = max(m, r.v[i][c] & 0x7FFFFFFFu);
+  auto p = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  m = max(uint32_t(p[0]), uint32_t(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  m = max(uint32_t(p[0]), uint32_t(p[1]));
+  if (m == 0) return 0;
+  const int ef = int(m >> 23);                 // an fp32 subnormal maximum counts as exponent -126
+  return (ef > 0 ? ef : 1) - 127 - 14;
+}
+
 template <int XF32>
-__device__ __forceinline__ void a_operands(const ARaw<XF32>& r, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
+__device__ __forceinline__ void a_operands(const ARaw<XF32>& r, int e, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int a = 16 * (j >> 1) + 4 * (j & 1) + p;
       if constexpr (XF32) {
-        // hi: x cut to fp16 precision (exact in fp16 for 2^-14 <= |x| < 65520);
-        // lo: the exact rest, rounded to fp16
-        const uint32_t u0 = r.v[a >> 2][a & 3], u1 = r.v[(a + 8) >> 2][(a + 8) & 3];
+        // scaled by 2^-e (exact unless far below the group's largest value); hi: cut to fp16
+        // precision (exact in fp16 for 2^-14 <= |x| < 65520); lo: the exact rest, rounded to fp16
+        const uint32_t u0 = __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(r.v[a >> 2][a & 3]), -e));
+        const uint32_t u1 =
+            __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(r.v[(a + 8) >> 2][(a + 8) & 3]), -e));
         const float h0 = __uint_as_float(u0 & 0xFFFFE000u), h1 = __uint_as_float(u1 & 0xFFFFE000u);
         hi[j][p] = pack_f16(h0, h1);
         lo[j][p] = pack_f16(__uint_as_float(u0) - h0, __uint_as_float(u1) - h1);
@@ -259,14 +282,25 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
       sc[t] = sr[t];
       if constexpr (kEarly) issue_w(t, gn);
     }
-    issue_a(g + 1);  // past g1 it reads zero
+    // the next group's activations go out now (past g1 they read zero); with two fp32 row blocks
+    // and 4-5 tiles, only once this group's have been turned into operands (registers)
+    constexpr bool kLateA = XF32 && MB == 2 && T >= 4;
+    if constexpr (!kLateA) issue_a(g + 1);
 
-    // activation operands and the group's -2^-14 sum_k x'
+    // activation operands and the group's -2^-14 sum_k x'; with fp32 activations, eo[mb][i] is
+    // the scale exponent of activation row 16 mb + 4 q + i, the row of accumulator element i
     u32x4 ahi[MB][4], alo[MB][4];
     floatx4 neg_sum[MB];
+    int eo[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      a_operands<XF32>(ac[mb], ahi[mb], alo[mb]);
+      int e = 0;
+      if constexpr (XF32) {
+        e = a_exponent(ac[mb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eo[mb][i] = __shfl(e, 4 * q + i);
+      }
+      a_operands<XF32>(ac[mb], e, ahi[mb], alo[mb]);
       neg_sum[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -274,6 +308,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
         if constexpr (XF32) neg_sum[mb] = mfma(alo[mb][j], neg_unit, neg_sum[mb]);
       }
     }
+    if constexpr (kLateA) issue_a(g + 1);
 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -297,7 +332,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(s, part[mb][i], acc[t][mb][i]);
+        for (int i = 0; i < 4; ++i) {
+          const float pv = XF32 ? __builtin_amdgcn_ldexpf(part[mb][i], eo[mb][i]) : part[mb][i];
+          acc[t][mb][i] = fmaf(s, pv, acc[t][mb][i]);
+        }
     }
   }
 

@@ -93,7 +93,7 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
   if (N == 0) return TB_OK;
   if (!packed || !scales || !xr || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr) || !aligned16(y)) return TB_ERR_ALIGN;
-  if (B >= tb::kWideMinBatch) {
+  if (B >= tb::wide_min_batch(packing, N, K)) {
     // one pass over the weights on the fp16 matrix cores
     tb::launch_gemv_wide(packing, packed, scales, xr, xr_dtype, y, int(B), int(N), int(K),
                          static_cast<hipStream_t>(stream));
@@ -135,6 +135,33 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
   return finish_launch();
 }
 
+int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K) {
+  if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return -1;
+  if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(B, 4 * K) ||
+      !fits(N, K))
+    return -1;
+  return B >= tb::wide_min_batch(packing, N, K) ? 4 * B * K : 0;
+}
+
+int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+                 const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+  const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
+  if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+  if (x_dtype != TB_F32 && x_dtype != TB_F16 && x_dtype != TB_BF16) return TB_ERR_DTYPE;
+  if (workspace_bytes < need) return TB_ERR_WORKSPACE;
+  if (N == 0) return TB_OK;
+  if (!packed || !scales || !x || !sign_bits || !y || !workspace) return TB_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y) ||
+      !aligned16(workspace))
+    return TB_ERR_ALIGN;
+  if (x == workspace) return TB_ERR_SHAPE;  // x' is written while x is read by other blocks
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  tb::launch_fwht(x, x_dtype, workspace, TB_F32, B, K, sign_bits, s);
+  tb::launch_gemv_wide(packing, packed, scales, workspace, TB_F32, y, int(B), int(N), int(K), s);
+  return finish_launch();
+}
+
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
@@ -168,6 +195,16 @@ int tb_ternarize(const float* w, int64_t N, int64_t K, const uint32_t* sign_bits
   return finish_launch();
 }
 
+int tb_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, void* stream) {
+  if (bytes < 0 || bytes > kMaxElems || bytes % 16 != 0) return TB_ERR_SHAPE;
+  if (bytes == 0) return TB_OK;
+  if (!src || !sink) return TB_ERR_NULL;
+  if (!aligned16(src) || !aligned16(sink)) return TB_ERR_ALIGN;
+  if (sink_words < tb::stream_read_grid(bytes)) return TB_ERR_WORKSPACE;
+  tb::launch_stream_read(static_cast<const uint8_t*>(src), bytes, sink, static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
 const char* tb_status_string(int status) {
   switch (status) {
     case TB_OK: return "ok";
@@ -177,6 +214,7 @@ const char* tb_status_string(int status) {
     case TB_ERR_DTYPE: return "dtype not accepted by this call";
     case TB_ERR_UNSUPPORTED: return "packing not accepted by this call";
     case TB_ERR_HIP: return "HIP runtime error at launch";
+    case TB_ERR_WORKSPACE: return "workspace smaller than tb_linear_workspace_bytes() asks for";
     default: return "unknown status";
   }
 }

@@ -11,7 +11,14 @@ constexpr int kGroup = 128;          // weights per fp16 scale
 constexpr int kBlock = 1024;         // rotation block size
 constexpr int kB3GroupBytes = 26;    // base-3 bytes per 128-group (25 full bytes + 3 trits and 2 pads)
 constexpr int kMaxBatch = 8;         // largest batch of the limb decode product (gemv.hip)
-constexpr int kWideMinBatch = 9;     // from this batch on, tb_gemv runs gemv_wide.hip
+// From this batch on, tb_gemv (and tb_linear_ws) run gemv_wide.hip instead of the limb kernel:
+// the measured crossover (fp32 x', weights streamed from HBM).  The limb kernel's cost grows with
+// B K (its limbs of x' live in LDS), the batched kernel's hardly with B, so long rows cross first.
+inline int wide_min_batch(int packing, int64_t n, int64_t k) {
+  if (k >= 8192) return 5;
+  if (n < 8192) return 7;
+  return packing == 0 ? 9 : 8;
+}
 constexpr int kWideMaxBatch = 32;    // largest batch of gemv_wide.hip
 constexpr int kWideGemmRows = 96;    // tb_gemm up to this M runs gemv_wide.hip in chunks of 32 rows
 
@@ -33,6 +40,8 @@ void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, c
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);
 void launch_ternarize(const float* w, int64_t n, int64_t k, const uint32_t* sign_bits, int8_t* trits,
                       uint16_t* scales, int32_t* bad_count, hipStream_t s);
+int stream_read_grid(int64_t bytes);
+void launch_stream_read(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 // Batch-1 base-3 decode product on independent matrix-core lane groups (decode1.hip): whether it
 // takes the shape, and the launch (x is x' when rotate is false, else the unrotated x).
 bool decode1_supports(int packing, int b, int n, int k);

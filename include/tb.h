@@ -43,16 +43,18 @@ typedef enum {
   TB_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                  */
   TB_ERR_DTYPE = 4,       /* dtype code not accepted by this call              */
   TB_ERR_UNSUPPORTED = 5, /* packing code not accepted by this call            */
-  TB_ERR_HIP = 6          /* the HIP runtime reported an error at launch       */
+  TB_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
+  TB_ERR_WORKSPACE = 7    /* a workspace is smaller than the call needs        */
 } tb_status;
 
 typedef enum { TB_PACK_2BIT = 0, TB_PACK_BASE3 = 1 } tb_packing;
 typedef enum { TB_F32 = 0, TB_F16 = 1, TB_BF16 = 2 } tb_dtype;
 
-/* Largest batch tb_gemv and tb_linear accept.  tb_gemv runs every batch in
- * one pass over the weights.  tb_linear runs up to TB_GEMV_KERNEL_BATCH rows
- * in one pass; a larger batch runs in chunks of TB_GEMV_KERNEL_BATCH rows,
- * each streaming the weights again. */
+/* Largest batch tb_gemv, tb_linear and tb_linear_ws accept.  tb_gemv and
+ * tb_linear_ws run every batch in one pass over the weights.  tb_linear (no
+ * workspace) runs up to TB_GEMV_KERNEL_BATCH rows in one pass; a larger batch
+ * runs in chunks of TB_GEMV_KERNEL_BATCH rows, each streaming the weights
+ * again. */
 #define TB_GEMV_MAX_BATCH 32
 #define TB_GEMV_KERNEL_BATCH 8
 
@@ -121,12 +123,12 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
  * xr: [B][K] rotated activations of xr_dtype (TB_F32 or TB_F16), read as
  * given; y: fp32 [B][N], overwritten.  1 <= B <= TB_GEMV_MAX_BATCH and
  * B * K * 4 < 2^31.
- * B <= TB_GEMV_KERNEL_BATCH: fp8 limbs of xr against fp4 codes, any
- * magnitude (a power-of-two scale per row and 128-group).
- * B > TB_GEMV_KERNEL_BATCH: fp16 matrix cores; fp32 xr is split into
- * fp16 hi + lo (about 2^-21 of |x| lost), so |xr| must stay below 65504
- * (larger values give inf or NaN), and values below 2^-14 keep an absolute
- * error of at most 2^-24 instead of a relative one.
+ * Small batches run fp8 (fp6 for base-3 at B = 1) limbs of xr against fp4
+ * codes; from B = 5 (K >= 8192), 7 (N < 8192), 8 (base-3) or 9 (2-bit) on,
+ * one pass on the fp16 matrix cores, fp32 xr split into fp16 hi + lo (about
+ * 2^-21 of |x| lost).  Both take any finite
+ * magnitude: xr gets a power-of-two scale per row and 128-group, undone in
+ * fp32 after the group's sum.
  * Accumulation is fp32 (not bit-reproducible across kernel versions). */
 int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
             int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, void* stream);
@@ -145,6 +147,26 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
  * followed by tb_gemv to fp32 accumulation order. */
 int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
               const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream);
+
+/* Workspace that tb_linear_ws needs for (packing, B, N, K): 4 B K bytes (x'
+ * in fp32) when that call runs on the batched matrix-core product, 0 when the
+ * one-launch fused kernel of tb_linear serves it; -1 for an unknown packing,
+ * B outside 1..TB_GEMV_MAX_BATCH, N < 0, K not a positive multiple of 1024 or
+ * sizes past 32-bit offsets.  Pure host function. */
+int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K);
+
+/* tb_linear with one pass over the weights at every batch: where the batch
+ * runs on the batched product (tb_linear_workspace_bytes > 0), x' = R_K x is
+ * written in fp32 to the caller's workspace and the product reads it, two
+ * launches on `stream`; otherwise exactly tb_linear.  Same pages, arguments
+ * and result as tb_linear, plus workspace: device memory of at least
+ * workspace_bytes >= tb_linear_workspace_bytes(packing, B, N, K) bytes (else
+ * TB_ERR_WORKSPACE), 16-byte aligned, owned by the caller, overwritten, and
+ * not overlapping x.  The library still allocates nothing.  Calls that share
+ * a workspace must be ordered (one stream). */
+int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+                 const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
+                 int64_t workspace_bytes, void* stream);
 
 /* Prefill product Y = X' W_hat^T for many rows: Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k].
  * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
@@ -185,6 +207,16 @@ int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const ui
  * w, scales (and sign_bits when given) 16-byte aligned. */
 int tb_ternarize(const float* w, int64_t N, int64_t K, const uint32_t* sign_bits, int8_t* trits,
                  uint16_t* scales, int32_t* bad_count, void* stream);
+
+/* Measurement aid, not part of the product path: read `bytes` bytes of device
+ * memory once (16-byte loads) and write one XOR word per workgroup to sink,
+ * which must hold TB_STREAM_SINK_WORDS uint32 (else TB_ERR_WORKSPACE).  The
+ * time of this call is the measured HBM read ceiling the weight-streaming
+ * products are compared with.  Pages: "Ternary Bonsai 2 27B release", section
+ * "Throughput" (decode is bound by the weight bytes read per token).
+ * 0 <= bytes < 2^31, a multiple of 16; src and sink 16-byte aligned. */
+#define TB_STREAM_SINK_WORDS 8192
+int tb_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
 
 /* Static text for a status code. */
 const char* tb_status_string(int status);

@@ -129,6 +129,41 @@ def test_gemm_validation():
     assert g(0, P, P, P, P, 0, 8, 128, None) == OK
 
 
+def test_linear_workspace_bytes():
+    lib = tb.library()
+    f = lib.tb_linear_workspace_bytes
+    # (packing, B, N, K): the fused one-launch kernel below the measured crossover, x' in fp32 above
+    assert f(0, 1, 17408, 5120) == 0 and f(1, 1, 17408, 5120) == 0
+    assert f(0, 8, 17408, 5120) == 0 and f(0, 9, 17408, 5120) == 4 * 9 * 5120
+    assert f(1, 7, 17408, 5120) == 0 and f(1, 8, 17408, 5120) == 4 * 8 * 5120
+    assert f(0, 6, 5120, 5120) == 0 and f(0, 7, 5120, 5120) == 4 * 7 * 5120
+    assert f(1, 4, 5120, 17408) == 0 and f(1, 5, 5120, 17408) == 4 * 5 * 17408
+    assert f(1, 32, 5120, 17408) == 4 * 32 * 17408
+    assert f(1, 33, 8, 1024) == -1 and f(1, 0, 8, 1024) == -1 and f(1, 4, 8, 1152) == -1
+    assert f(2, 4, 8, 1024) == -1 and f(1, 4, -1, 1024) == -1
+
+
+def test_linear_ws_validation():
+    lib = tb.library()
+    g = lib.tb_linear_ws
+    # (packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, workspace, workspace_bytes, stream)
+    need = 4 * 16 * 1024
+    assert g(3, P, P, P, 2, P, P, 16, 8, 1024, P, need, None) == UNSUP
+    assert g(1, P, P, P, 2, P, P, 33, 8, 1024, P, need, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, 16, 8, 1152, P, need, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, 16, -8, 1024, P, need, None) == SHAPE
+    assert g(1, P, P, P, 3, P, P, 16, 8, 1024, P, need, None) == DTYPE
+    assert g(1, P, P, P, 2, P, P, 16, 8, 1024, P, need - 1, None) == 7   # TB_ERR_WORKSPACE
+    assert g(1, P, P, P, 2, P, P, 16, 8, 1024, None, need, None) == NULL
+    assert g(1, P, P, P, 2, None, P, 16, 8, 1024, P, need, None) == NULL
+    assert g(1, P, P, P, 2, P, P, 16, 8, 1024, MIS, need, None) == ALIGN
+    assert g(1, P, P, P, 2, P, P, 16, 8, 1024, P, need, None) == SHAPE   # x is the workspace
+    assert g(1, P, P, P, 2, P, P, 16, 0, 1024, P + 0x100000, need, None) == OK   # empty
+    # batches the fused kernel serves need no workspace and behave as tb_linear
+    assert g(1, P, P, P, 3, P, P, 1, 8, 1024, None, 0, None) == DTYPE
+    assert g(1, P, P, P, 2, P, P, 1, 0, 1024, None, 0, None) == OK
+
+
 def test_ternarize_validation():
     lib = tb.library()
     g = lib.tb_ternarize
@@ -146,10 +181,23 @@ def test_ternarize_validation():
     assert g(None, 0, 1024, None, None, None, None, None) == OK   # empty call
 
 
+def test_stream_read_validation():
+    lib = tb.library()
+    g = lib.tb_stream_read
+    assert g(P, -1, P, 8192, None) == SHAPE
+    assert g(P, 1 << 31, P, 8192, None) == SHAPE
+    assert g(P, 1000, P, 8192, None) == SHAPE         # not a multiple of 16
+    assert g(None, 1024, P, 8192, None) == NULL
+    assert g(P, 1024, None, 8192, None) == NULL
+    assert g(MIS, 1024, P, 8192, None) == ALIGN
+    assert g(P, 1 << 30, P, 100, None) == 7          # the sink is too small for the grid
+    assert g(None, 0, None, 0, None) == OK
+
+
 def test_status_strings():
     lib = tb.library()
-    for st in range(7):
-        assert lib.tb_status_string(st)
+    for st in range(8):
+        assert lib.tb_status_string(st) != b"unknown status"
     assert lib.tb_status_string(99) == b"unknown status"
     assert lib.tb_last_hip_error() == b""
 

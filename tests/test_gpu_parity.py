@@ -164,6 +164,10 @@ def _e2e_gemv(wid, packing, n, k, x_dtype, outliers, batches, layer=0, linear=0)
             y1 = host(tb.tb_linear(packing, packed, sd, xd[:b].contiguous(), sgn))
             e1 = oracle.rel_err(y1, want[:b])
             assert e1 < TOL, ("tb_linear", b, e1)
+            # one pass over the weights at any batch, x' through a workspace
+            y2 = host(tb.tb_linear_ws(packing, packed, sd, xd[:b].contiguous(), sgn))
+            e2 = oracle.rel_err(y2, want[:b])
+            assert e2 < TOL, ("tb_linear_ws", b, e2)
     return errs
 
 
@@ -217,29 +221,35 @@ def test_linear_fused_rotation(packing, n, k, x_dtype):
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("exp2", [-120, 100])
 def test_gemv_extreme_magnitudes(packing, exp2):
-    """Activations scaled by 2^exp2 (exactly).  At 2^-120 every group's
-    power-of-two scale hits its upper clamp (the limb exponents must stay
-    valid E8M0 values); at 2^100 the scale is far negative.  The error bound
-    is relative to the row rms, so it is the same at any scale."""
+    """Activations scaled by 2^exp2 (exactly), at every product path: the limb
+    kernels (batch 1..8; at 2^-120 every group's power-of-two scale hits its
+    upper clamp, at 2^100 it is far negative) and the fp16 matrix-core kernel
+    (batch 6/9..32), whose per-row-and-group power-of-two scale brings x'
+    into the fp16 range first.  The error bound is relative to the row rms,
+    so it is the same at any scale."""
     n, k = 300, 5120
     note(f"gemv/linear {packing} x * 2^{exp2}")
     g = synth.rng(250, 0, exp2 & 255, 0)
     t = synth.trits(g, n, k)
     s = synth.scales_f16(g, n, k)
     signs = synth.sign_bits(g, k)
-    x32 = np.ldexp(g.standard_normal((4, k)), exp2).astype(np.float32)
+    x32 = np.ldexp(g.standard_normal((tb.TB_GEMV_MAX_BATCH, k)), exp2).astype(np.float32)
     assert np.all(np.isfinite(x32)) and np.min(np.abs(x32[x32 != 0])) > 0
     x64 = x32.astype(np.float64)
     packed, _ = PACK_REF[packing](t)
-    pd, sd, xd = dev(packed), scales_dev(s), dev(x32)
+    pd, sd, xd, sgn = dev(packed), scales_dev(s), dev(x32), signs_dev(signs)
     # x' given: the exact rotation of the fp32 activations, rounded to fp32
     xr = oracle.rotate(x64, signs)
     want = oracle.gemv(packing, packed, s, xr, k)
-    got = host(tb.tb_gemv(packing, pd, sd, dev(xr.astype(np.float32))))
-    assert oracle.rel_err(got, want) < TOL
-    # rotation fused
-    got = host(tb.tb_linear(packing, pd, sd, xd, signs_dev(signs)))
-    assert oracle.rel_err(got, want) < TOL
+    xrd = dev(xr.astype(np.float32))
+    for b in (1, 4, 6, 8, 9, 17, tb.TB_GEMV_MAX_BATCH):
+        got = host(tb.tb_gemv(packing, pd, sd, xrd[:b].contiguous()))
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_gemv", b)
+        # rotation fused, or through the workspace
+        got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear", b)
+        got = host(tb.tb_linear_ws(packing, pd, sd, xd[:b].contiguous(), sgn))
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear_ws", b)
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
@@ -270,10 +280,11 @@ def test_gemv_batches_9_to_32_one_pass(packing, n, k, xr_dtype):
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 def test_gemv_batches_9_to_32_magnitudes(packing):
-    """The one-pass path carries fp32 x' as fp16 hi + lo: relative error
-    stays at the fp32 level up to |x'| near 65504 (largest value 60000), and
-    for tiny activations (|x'| ~ 2^-20, below the fp16 normal range) the
-    error per output stays within sum_k |s t| 2^-24."""
+    """The one-pass path carries fp32 x' as fp16 hi + lo after a power-of-two
+    scale per activation row and group: the relative error stays at the fp32
+    level at any magnitude, including values past the fp16 range (1e30), far
+    below its normal range (2^-20, and 2^-120 with fp32 subnormals), rows of very
+    different size in one call, and groups that are all zero."""
     n, k = 300, 2048
     note(f"gemv wide {packing} magnitudes")
     g = synth.rng(223, 0, 0, 0)
@@ -281,17 +292,22 @@ def test_gemv_batches_9_to_32_magnitudes(packing):
     s = synth.scales_f16(g, n, k)
     packed, _ = PACK_REF[packing](t)
     pd, sd = dev(packed), scales_dev(s)
-    big = g.standard_normal((16, k))
-    big = (big * (60000.0 / np.abs(big).max())).astype(np.float32)
-    want = oracle.gemv(packing, packed, s, big.astype(np.float64), k)
-    got = host(tb.tb_gemv(packing, pd, sd, dev(big)))
-    assert oracle.rel_err(got, want) < 1e-5
-    tiny = np.ldexp(g.standard_normal((16, k)), -20).astype(np.float32)
-    want = oracle.gemv(packing, packed, s, tiny.astype(np.float64), k)
-    got = host(tb.tb_gemv(packing, pd, sd, dev(tiny)))
-    w = t.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
-    bound = np.abs(w).sum(axis=1) * 2.0 ** -24
-    assert np.all(np.abs(got - want) <= bound[None, :] * 1.01 + 1e-6 * np.abs(want))
+    base = g.standard_normal((16, k))
+    cases = {
+        "near fp16 max": base * (60000.0 / np.abs(base).max()),
+        "1e30": base * 1e30,
+        "2^-20": np.ldexp(base, -20),
+        "2^-120": np.ldexp(base, -120),          # the smallest entries are fp32 subnormals
+        "mixed rows": base * np.ldexp(1.0, np.arange(16)[:, None] * 16 - 120),
+        "zero groups": base * (np.arange(k)[None, :] // 128 % 3 != 1),
+    }
+    for name, x in cases.items():
+        x32 = x.astype(np.float32)
+        want = oracle.gemv(packing, packed, s, x32.astype(np.float64), k)
+        got = host(tb.tb_gemv(packing, pd, sd, dev(x32)))
+        err = oracle.rel_err(got, want)
+        note(f"  {name}: rel err {err:.2e}")
+        assert err < 1e-5, (name, err)
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
@@ -318,6 +334,15 @@ def test_gemv_linear_batches_above_8(packing):
         assert oracle.rel_err(got, want[:b]) < TOL, ("tb_gemv", b)
         got = host(tb.tb_linear(packing, pd, sd, xd[:b].contiguous(), sgn))
         assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear", b)
+    # tb_linear_ws: one caller workspace of the largest size, reused by every batch in turn
+    ws = torch.empty(tb.tb_linear_workspace_bytes(packing, tb.TB_GEMV_MAX_BATCH, n, k), dtype=torch.uint8,
+                     device="cuda")
+    for b in (1, 2, 5, 6, 8, 9, 16, 21, tb.TB_GEMV_MAX_BATCH, 7, 1):
+        got = host(tb.tb_linear_ws(packing, pd, sd, xd[:b].contiguous(), sgn, workspace=ws))
+        assert oracle.rel_err(got, want[:b]) < TOL, ("tb_linear_ws", b)
+    need = tb.tb_linear_workspace_bytes(packing, 16, n, k)
+    with pytest.raises(tb.TBError, match="workspace"):
+        tb.tb_linear_ws(packing, pd, sd, xd[:16].contiguous(), sgn, workspace=ws[:need - 16])
 
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
@@ -405,3 +430,20 @@ def test_gemm_base3_equals_2bit():
     y2 = host(tb.tb_gemm("2bit", p2, s, xr[:20].contiguous()))
     y3 = host(tb.tb_gemm("base3", p3, s, xr[:20].contiguous()))
     assert np.array_equal(y2, y3)
+
+
+# ------------------------------------------------------------------ measurement aid
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 32768 + 48, 19496960, 300 << 20])
+def test_stream_read_touches_every_word_once(nbytes):
+    """The read-ceiling kernel reads each 32-bit word exactly once: the XOR of its
+    per-workgroup words equals the XOR of the buffer (every word distinct here)."""
+    note(f"stream read {nbytes} bytes")
+    words = nbytes // 4
+    g = synth.rng(270, 0, nbytes % 251, 0)
+    host_buf = g.integers(0, 2 ** 32, size=words, dtype=np.uint64).astype(np.uint32)
+    buf = dev(host_buf.view(np.int32))
+    sink = torch.zeros(tb.TB_STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    tb.tb_stream_read(buf, sink)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host_buf)
