@@ -24,7 +24,8 @@ TB_STREAM_SINK_WORDS = 8192
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",
-           "tb_gemv", "tb_linear", "tb_linear_workspace_bytes", "tb_linear_ws", "tb_gemm", "tb_ternarize",
+           "tb_gemv", "tb_linear", "tb_linear_workspace_bytes", "tb_linear_ws", "tb_linear_noalloc", "tb_gemm",
+           "tb_ternarize",
            "tb_stream_read", "tb_status_string", "tb_last_hip_error")
 
 _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -38,6 +39,7 @@ _SIGNATURES = {
     "tb_linear": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_linear_workspace_bytes": (_I64, [_INT, _I64, _I64, _I64]),
     "tb_linear_ws": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP]),
+    "tb_linear_noalloc": (_INT, [_INT, _VP, _VP, _VP, _INT, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_gemm": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_ternarize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "tb_stream_read": (_INT, [_VP, _I64, _VP, _I64, _VP]),
@@ -264,6 +266,21 @@ def tb_linear_ws(packing, packed, scales, x, sign_bits, workspace=None, y=None, 
     _shape(y, "y", (b, n))
     _call("tb_linear_ws", _packing(packing), _ptr(packed), _ptr(scales), _ptr(x), _ACT_DT[x.dtype],
           _ptr(sign_bits), _ptr(y), b, n, k, _ptr(workspace), ws_bytes, _stream(stream))
+    return y
+
+
+def tb_linear_noalloc(packing, packed, scales, x, sign_bits, y, stream=None):
+    """tb_linear_ws with x' in the library's static device scratch: no allocation anywhere
+    (y must be given)."""
+    _check(x, "x", tuple(_ACT_DT))
+    _rank2(x, "x")
+    b, k = x.shape
+    n = _weights(packing, packed, scales, k)
+    _signs(sign_bits, k)
+    _check(y, "y", (torch.float32,))
+    _shape(y, "y", (b, n))
+    _call("tb_linear_noalloc", _packing(packing), _ptr(packed), _ptr(scales), _ptr(x), _ACT_DT[x.dtype],
+          _ptr(sign_bits), _ptr(y), b, n, k, _stream(stream))
     return y
 
 

@@ -162,6 +162,21 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
   return finish_launch();
 }
 
+int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+                      const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream) {
+  const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
+  if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+  if (need > 4 * tb::kStaticScratchFloats) return TB_ERR_SCRATCH;
+  void* scratch = nullptr;
+  const hipError_t e = tb::static_scratch(&scratch);
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s (static scratch lookup)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return TB_ERR_HIP;
+  }
+  return tb_linear_ws(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, scratch, need, stream);
+}
+
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
@@ -215,6 +230,7 @@ const char* tb_status_string(int status) {
     case TB_ERR_UNSUPPORTED: return "packing not accepted by this call";
     case TB_ERR_HIP: return "HIP runtime error at launch";
     case TB_ERR_WORKSPACE: return "workspace smaller than tb_linear_workspace_bytes() asks for";
+    case TB_ERR_SCRATCH: return "the call needs more than the library's static scratch (4 MiB: B K <= 2^20)";
     default: return "unknown status";
   }
 }

@@ -40,6 +40,11 @@ void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, c
                    const uint32_t* sign_bits, float* y, int b, int n, int k, hipStream_t s);
 void launch_ternarize(const float* w, int64_t n, int64_t k, const uint32_t* sign_bits, int8_t* trits,
                       uint16_t* scales, int32_t* bad_count, hipStream_t s);
+// The static device buffer of tb_linear_noalloc (noalloc.hip): 4 MiB, x' of up to 32 rows of
+// K = 32768 in fp32.  static_scratch gives the current device's address of it (looked up once
+// per device).
+constexpr int64_t kStaticScratchFloats = int64_t(1) << 20;
+hipError_t static_scratch(void** ptr);
 int stream_read_grid(int64_t bytes);
 void launch_stream_read(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 // Batch-1 base-3 decode product on independent matrix-core lane groups (decode1.hip): whether it

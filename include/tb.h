@@ -44,7 +44,8 @@ typedef enum {
   TB_ERR_DTYPE = 4,       /* dtype code not accepted by this call              */
   TB_ERR_UNSUPPORTED = 5, /* packing code not accepted by this call            */
   TB_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
-  TB_ERR_WORKSPACE = 7    /* a workspace is smaller than the call needs        */
+  TB_ERR_WORKSPACE = 7,   /* a workspace is smaller than the call needs        */
+  TB_ERR_SCRATCH = 8      /* the call needs more than the static scratch holds */
 } tb_status;
 
 typedef enum { TB_PACK_2BIT = 0, TB_PACK_BASE3 = 1 } tb_packing;
@@ -167,6 +168,21 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K);
 int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
                  const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
                  int64_t workspace_bytes, void* stream);
+
+/* tb_linear_ws without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Where
+ * tb_linear_workspace_bytes(packing, B, N, K) > 0, x' goes to a static device
+ * array of the library (4 MiB per GPU, held until the process ends) instead of
+ * a caller workspace; the call returns TB_ERR_SCRATCH when it would need more
+ * (B K > 2^20 floats).  Otherwise it is exactly tb_linear.  Same arguments,
+ * kernels and result as tb_linear_ws.  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (different streams without ordering,
+ * or several host threads) race on it; order them on one stream.  x' is fully
+ * written before it is read, so no clearing is needed between calls.  The
+ * first call on a device looks the array's address up (no allocation). */
+int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+                      const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream);
 
 /* Prefill product Y = X' W_hat^T for many rows: Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k].
  * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights

@@ -164,6 +164,17 @@ def test_linear_ws_validation():
     assert g(1, P, P, P, 2, P, P, 1, 0, 1024, None, 0, None) == OK
 
 
+def test_linear_noalloc_validation():
+    lib = tb.library()
+    g = lib.tb_linear_noalloc
+    # (packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream): errors before any device call
+    assert g(3, P, P, P, 2, P, P, 16, 8, 1024, None) == UNSUP
+    assert g(1, P, P, P, 2, P, P, 33, 8, 1024, None) == SHAPE
+    assert g(1, P, P, P, 2, P, P, 32, 8, 1 << 16, None) == 8          # B K = 2^21 > the static 2^20 floats
+    assert g(1, P, P, P, 3, P, P, 1, 8, 1024, None) == DTYPE          # batch the fused kernel serves
+    assert g(1, P, P, P, 2, None, P, 1, 8, 1024, None) == NULL
+
+
 def test_ternarize_validation():
     lib = tb.library()
     g = lib.tb_ternarize
@@ -196,7 +207,7 @@ def test_stream_read_validation():
 
 def test_status_strings():
     lib = tb.library()
-    for st in range(8):
+    for st in range(9):
         assert lib.tb_status_string(st) != b"unknown status"
     assert lib.tb_status_string(99) == b"unknown status"
     assert lib.tb_last_hip_error() == b""

@@ -1,0 +1,60 @@
+"""The entry point that allocates nothing (tb_linear_noalloc) against the one with a caller
+workspace (tb_linear_ws), through the C ABI, on two calls in a row, the second smaller."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import fwht_rotation_sqrt_amd as tb
+import oracle
+import synth
+from gpu_util import TOL, dev, host, note, scales_dev, signs_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(packing, n, k, rows, seed):
+    g = synth.rng(290, seed, n % 251, k // 1024)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x = g.standard_normal((rows, k)).astype(np.float32)
+    packed, _ = (oracle.pack_2bit if packing == "2bit" else oracle.pack_base3)(t)
+    want = oracle.gemv(packing, packed, s, oracle.rotate(x.astype(np.float64), signs), k)
+    return dev(packed), scales_dev(s), dev(x), signs_dev(signs), want
+
+
+def _noalloc(packing, pd, sd, xd, sgn, y):
+    lib = tb.library()
+    b, k = xd.shape
+    n = pd.shape[0]
+    st = lib.tb_linear_noalloc(tb.PACKINGS[packing], ctypes.c_void_p(pd.data_ptr()), ctypes.c_void_p(sd.data_ptr()),
+                               ctypes.c_void_p(xd.data_ptr()), tb.TB_F32, ctypes.c_void_p(sgn.data_ptr()),
+                               ctypes.c_void_p(y.data_ptr()), b, n, k,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, tb.TBError("tb_linear_noalloc", st)
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_noalloc_matches_workspace_entry_point(packing):
+    # call 1: 32 rows of K = 17408 (2.2 MB of the 4 MiB scratch); call 2: 9 rows of K = 3072
+    for (n, k, rows), seed in (((300, 17408, 32), 0), ((200, 3072, 9), 1)):
+        note(f"noalloc {packing} n={n} k={k} rows={rows}")
+        pd, sd, xd, sgn, want = _case(packing, n, k, rows, seed)
+        assert tb.tb_linear_workspace_bytes(packing, rows, n, k) > 0   # the call uses the scratch
+        y0 = torch.full((rows, n), float("nan"), dtype=torch.float32, device="cuda")
+        _noalloc(packing, pd, sd, xd, sgn, y0)
+        y1 = tb.tb_linear_ws(packing, pd, sd, xd, sgn)
+        a, b = host(y0), host(y1)
+        assert np.array_equal(a, b)                                     # same kernels, same x'
+        assert oracle.rel_err(a, want) < TOL
+
+
+def test_noalloc_small_batches_and_limit():
+    pd, sd, xd, sgn, want = _case("base3", 64, 2048, 4, 2)
+    y = torch.empty((4, 64), dtype=torch.float32, device="cuda")
+    _noalloc("base3", pd, sd, xd, sgn, y)                              # the fused kernel, no scratch
+    assert oracle.rel_err(host(y), want) < TOL
+    lib = tb.library()
+    assert lib.tb_linear_noalloc(1, 16, 16, 16, 0, 16, 16, 32, 8, 1 << 16, None) == 8  # beyond 4 MiB
