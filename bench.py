@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-token", action="store_true", help="skip the 64-layer decode token leg")
     ap.add_argument("--no-stream", action="store_true", help="skip the read-ceiling leg")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="do not start rocm-smi for the shader clock (for runs under a counter profiler, whose "
+                         "preloaded library would make the child's interpreter start an exec after GPU init)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating HBM byte counters) and exit")
     ap.add_argument("--gemv-batch", type=int, metavar="B",
@@ -141,7 +144,7 @@ def decode_setup():
                 per_copy=per_copy, copies=copies)
 
 
-def bench_decode(d, steps, warmup):
+def bench_decode(d, steps, warmup, smi=True):
     packed, scales, copies = d["packed"], d["scales"], d["copies"]
 
     def step(i):
@@ -174,10 +177,12 @@ def bench_decode(d, steps, warmup):
     t_gemv = event_time(g_gemv) / steps
     t_rot = event_time(g_rot) / steps
     # the shader clock while the product runs: about 3 s of replays queued, rocm-smi read meanwhile
-    for _ in range(max(1, int(3.0 / max(t_fused * steps, 1e-6)))):
-        g_fused.replay()
-    sclk = shader_clock()
-    torch.cuda.synchronize()
+    sclk = "not read (--no-smi)"
+    if smi:
+        for _ in range(max(1, int(3.0 / max(t_fused * steps, 1e-6)))):
+            g_fused.replay()
+        sclk = shader_clock()
+        torch.cuda.synchronize()
     return wall, t_fused, t_gemv, t_rot, sclk
 
 
@@ -475,7 +480,7 @@ def run_suite(path, argv):
                   flush=True)
     tok = suite_token(gen)
     print(f"token: fused {tok['fused'] * 1e3:.3f} ms, separate {tok['separate'] * 1e3:.3f} ms", flush=True)
-    sclk = shader_clock()
+    sclk = shader_clock() if "--no-smi" not in argv else "not read (--no-smi)"
 
     pk = HBM_PEAK_GBS
     lines.append("# Block linears and the 64-layer decode token stream (MI355X, one GPU)")
@@ -594,7 +599,7 @@ def main():
         print(json.dumps(bench_gemv_batch(args.gemv_batch, args.steps)), flush=True)
         return
     d = decode_setup()
-    wall, t_fused, t_gemv, t_rot, sclk = bench_decode(d, args.steps, args.warmup)
+    wall, t_fused, t_gemv, t_rot, sclk = bench_decode(d, args.steps, args.warmup, not args.no_smi)
     ms_per_step = wall / args.steps * 1e3
     per_copy = d["per_copy"]
     value = per_copy / (wall / args.steps) / 1e9
