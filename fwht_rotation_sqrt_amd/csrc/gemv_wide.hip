@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
                                                             int nb, int n, int k) {
   constexpr int kGroupBytes = PACK == 0 ? 32 : kB3GroupBytes;
   constexpr int kXsz = XF32 ? 4 : 2;
-  constexpr uint32_t kTab = PACK == 1 ? kTableBytes : 0;  // reduction area follows the table
+  constexpr uint32_t kTab = 0;  // the reduction area reuses the table's LDS once every wave has left the loop
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, q = lane >> 4;
   const int groups = k / kGroup;
   const uint32_t row_bytes = uint32_t(groups) * kGroupBytes;
@@ -340,6 +340,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   }
 
   // partial sums of the waves -> LDS -> added in wave order -> y
+  if constexpr (PACK == 1) {  // the table is overwritten: every wave must be past its last lookup
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -362,7 +367,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
 template <int PACK, int XF32, int MB, int T>
 void run(const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k, hipStream_t s) {
   constexpr int NW = kWaves;
-  constexpr int lds = (PACK == 1 ? kTableBytes : 0) + NW * T * MB * kRedSlot;
+  constexpr int kRed = NW * T * MB * kRedSlot;
+  constexpr int lds = PACK == 1 && kTableBytes > kRed ? kTableBytes : kRed;
   static const bool attr = [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_wide_kernel<PACK, XF32, MB, T, NW>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -388,8 +394,10 @@ void run_t(int t, const uint8_t* p, const uint16_t* sc, const void* x, float* y,
 template <int PACK>
 void run_pack(int xr_dt, const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k,
               hipStream_t s) {
-  // tiles per workgroup: the fewest that keep the grid within one workgroup
-  // per compute unit (at most 5)
+  // tiles per workgroup: the fewest that keep the grid within one workgroup per compute unit
+  // (at most 5); two workgroups per unit with fewer tiles each ran 20-80 % slower at every shape
+  // and batch (each workgroup fetches the whole activation block, and the operands built from it
+  // serve fewer tiles)
   const int tiles = (n + 15) / 16;
   const int t = std::min(5, std::max(1, (tiles + 255) / 256));
   const bool f32 = xr_dt == 0;
