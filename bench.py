@@ -400,9 +400,37 @@ def suite_token(gen, layers=64, reps=10, per_call=True):
                 if prod:
                     tb.tb_gemv("base3", p, s, xr[k], y=ys[j])
 
+    # The same layers with true dependencies: each call's input is the previous call's output (the
+    # first K values of it), per call (dependent) or with q/k/v -> o -> gate/up in one
+    # tb_decode_chain launch and down after it (chained: two launches per layer).
+    F3, H3 = 2 * F, 3 * H
+    yq = torch.empty((1, H3), dtype=torch.float32, device="cuda")
+    yo = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    yg = torch.empty((1, F3), dtype=torch.float32, device="cuda")
+    yd = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    x_first = W[0][0][2]
+    sync = torch.zeros(tb.TB_CHAIN_MAX + 2, dtype=torch.int32, device="cuda")
+
+    def dependent():
+        x = x_first
+        for (pq, sq, _), (po, so, _), (pg, sgg, _), (pd, sd, _) in W:
+            tb.tb_linear("base3", pq, sq, x, sg[H], y=yq)
+            tb.tb_linear("base3", po, so, yq[:, :H], sg[H], y=yo)
+            tb.tb_linear("base3", pg, sgg, yo, sg[H], y=yg)
+            tb.tb_linear("base3", pd, sd, yg[:, :F], sg[F], y=yd)
+            x = yd
+
+    def chained():
+        x = x_first
+        for (pq, sq, _), (po, so, _), (pg, sgg, _), (pd, sd, _) in W:
+            tb.tb_decode_chain("base3", [(pq, sq), (po, so), (pg, sgg)], x, sg[H], sync, ys=[yq[0], yo[0], yg[0]])
+            tb.tb_linear("base3", pd, sd, yg[:, :F], sg[F], y=yd)
+            x = yd
+
     res = {"bytes": total, "layers": layers, "calls_fused": 4 * layers}
     for name, fn in (("fused", fused), ("separate", separate),
-                     ("rotate_only", lambda: separate(True, False)), ("gemv_only", lambda: separate(False, True))):
+                     ("rotate_only", lambda: separate(True, False)), ("gemv_only", lambda: separate(False, True)),
+                     ("dependent", dependent), ("chained", chained)):
         _, g = time_graph(fn, fn)
         res[name] = event_time(g, reps)
         del g
@@ -530,6 +558,10 @@ def run_suite(path, argv):
                  f"{1 / t_s:.1f} tokens/s-equivalent.")
     lines.append(f"- Rotation alone (256 calls): {t_r * 1e3:.3f} ms; products alone: {t_g * 1e3:.3f} ms; "
                  f"FWHT share of the separate route = {100 * t_r / (t_r + t_g):.1f} %.")
+    lines.append(f"- With true dependencies (each call's input = the previous call's output): "
+                 f"{tok['dependent'] * 1e3:.3f} ms per token = {1 / tok['dependent']:.1f} tokens/s with 256 "
+                 f"tb_linear calls; {tok['chained'] * 1e3:.3f} ms = **{1 / tok['chained']:.1f} tokens/s** with "
+                 f"q/k/v -> o -> gate/up in one tb_decode_chain launch per layer (128 launches).")
     lines.append("")
     lines.append("| call | N x K | us per call (fused) | GB/s |")
     lines.append("|---|---|---|---|")
@@ -663,13 +695,18 @@ def main():
         t_f, t_r, t_g = token["fused"], token["rotate_only"], token["gemv_only"]
         rec["decode_token_64_layers"] = {
             "tokens_per_s_equiv": round(1.0 / t_f, 1), "ms_per_token": round(t_f * 1e3, 4),
+            "dependent_tokens_per_s": round(1.0 / token["dependent"], 1),
+            "chained_tokens_per_s": round(1.0 / token["chained"], 1),
+            "chained_launches_per_token": 2 * token["layers"],
             "weight_bytes_per_token": token["bytes"], "gbs": round(token["bytes"] / t_f / 1e9, 1),
             "frac_of_hbm_peak": round(token["bytes"] / t_f / 1e9 / HBM_PEAK_GBS, 4),
             "calls_per_token": token["calls_fused"],
             "separate_route_ms": round(token["separate"] * 1e3, 4),
             "fwht_share_of_separate_route": round(t_r / (t_r + t_g), 4),
             "workload": "64 layers x (qkv 15360x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408), "
-                        "base-3, batch 1, tb_linear per call, one HIP graph"}
+                        "base-3, batch 1, one HIP graph; tokens_per_s_equiv: tb_linear per call on fixed inputs; "
+                        "dependent: each call's input is the previous output; chained: the same with "
+                        "qkv -> o -> gate_up in one tb_decode_chain launch per layer"}
     print(json.dumps(rec), flush=True)
 
 

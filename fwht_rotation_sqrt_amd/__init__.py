@@ -21,11 +21,18 @@ TB_F32, TB_F16, TB_BF16 = 0, 1, 2
 TB_GEMV_MAX_BATCH = 32   # tb_gemv: one pass over the weights at any batch up to this
 TB_GEMV_KERNEL_BATCH = 8  # tb_linear above this: chunks of 8 rows, each re-streaming the weights
 TB_STREAM_SINK_WORDS = 8192
+TB_CHAIN_MAX = 8
+
+
+class ChainLinear(ctypes.Structure):
+    """tb_chain_linear: one linear of a tb_decode_chain call."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64)]
 PACKINGS = {"2bit": TB_PACK_2BIT, "base3": TB_PACK_BASE3}
 
 EXPORTS = ("tb_packed_row_bytes", "tb_pack_2bit", "tb_pack_base3", "tb_unpack", "tb_fwht_rotate",
            "tb_gemv", "tb_linear", "tb_linear_workspace_bytes", "tb_linear_ws", "tb_linear_noalloc", "tb_gemm",
-           "tb_ternarize",
+           "tb_ternarize", "tb_decode_chain",
            "tb_stream_read", "tb_status_string", "tb_last_hip_error")
 
 _VP, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -43,6 +50,7 @@ _SIGNATURES = {
     "tb_gemm": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP]),
     "tb_ternarize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "tb_stream_read": (_INT, [_VP, _I64, _VP, _I64, _VP]),
+    "tb_decode_chain": (_INT, [_INT, _VP, _INT, _VP, _INT, _VP, _I64, _VP, _I64, _INT, _VP]),
     "tb_status_string": (ctypes.c_char_p, [_INT]),
     "tb_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -333,3 +341,29 @@ def tb_stream_read(src, sink, nbytes=None, stream=None):
     if not 0 <= nbytes <= total:
         raise ValueError(f"nbytes = {nbytes} outside 0..{total}")
     _call("tb_stream_read", _ptr(src), nbytes, _ptr(sink), sink.numel(), _stream(stream))
+
+
+def tb_decode_chain(packing, linears, x0, sign_bits, sync, ys=None, spin_limit=0, stream=None):
+    """Dependent batch-1 linears in one launch: linears = [(packed, scales), ...]; linear i > 0 reads
+    the first K outputs of linear i - 1.  sync: int32 device tensor of at least len(linears) + 2
+    words, zero before the first call.  Returns the outputs [y_0, ...] (fp32 [N_i])."""
+    _check(x0, "x0", tuple(_ACT_DT))
+    k = x0.numel()
+    if x0.dim() not in (1, 2) or (x0.dim() == 2 and x0.shape[0] != 1):
+        raise ValueError(f"x0 must be one activation row, got shape {tuple(x0.shape)}")
+    _signs(sign_bits, k)
+    _check(sync, "sync", (torch.int32,))
+    if not 1 <= len(linears) <= TB_CHAIN_MAX:
+        raise ValueError(f"1..{TB_CHAIN_MAX} linears, got {len(linears)}")
+    arr = (ChainLinear * len(linears))()
+    outs = []
+    for i, (packed, scales) in enumerate(linears):
+        n = _weights(packing, packed, scales, k)
+        y = ys[i] if ys is not None else torch.empty(n, dtype=torch.float32, device=x0.device)
+        _check(y, "y", (torch.float32,))
+        _shape(y, "y", (n,))
+        arr[i] = ChainLinear(packed.data_ptr(), scales.data_ptr(), y.data_ptr(), n)
+        outs.append(y)
+    _call("tb_decode_chain", _packing(packing), ctypes.cast(arr, ctypes.c_void_p), len(linears), _ptr(x0),
+          _ACT_DT[x0.dtype], _ptr(sign_bits), k, _ptr(sync), sync.numel(), int(spin_limit), _stream(stream))
+    return outs

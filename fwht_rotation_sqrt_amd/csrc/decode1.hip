@@ -248,11 +248,6 @@ __device__ __forceinline__ void build_record(uint32_t xb, int g, int s, uint32_t
   }
 }
 
-// Phase timestamps of a profiling build (compiled out here).
-#ifndef D1_TS
-#define D1_TS(i)
-#endif
-
 // 4x4 transpose of 16-byte pieces across the four lane groups: on entry lane group a holds in
 // r[b] (b = 0..3) piece a of quarter b's 64-byte chunk; on exit it holds in r[b] piece b of its own
 // quarter a.  Two rounds of lane swaps: across lane bit 5 (lane group bit 1), then lane bit 4.
@@ -275,90 +270,82 @@ __device__ __forceinline__ void transpose_pieces(u32x4 (&r)[4]) {
     }
 }
 
-// Kernel.  Grid: one workgroup per run of consecutive 16-row tiles (workgroup w takes tiles
-// [w T / G, (w + 1) T / G)).  Waves 0 .. kPrep - 1 prepare the activations (kPrep = K / 1024, one
-// 1024-block each: rotation, then the records of the block's 8 groups).  Each tile has HALVES
-// waves after them; lane group kb of a tile's wave h walks groups h G4 / HALVES .. of quarter kb
-// of the tile's 16 rows (G4 = K / 512 groups per quarter, even, so each quarter starts on a
-// 4-byte boundary), and the halves' partial sums meet in LDS.
-template <int G4, int HALVES, int XDT, bool ROT>
-__global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, const void* __restrict__ x,
-    const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int n, int tiles, int nslots, int grid, int nthreads) {
+// The activation part of one linear, for activation wave `wave`: block `wave` of x (one of K/1024),
+// rotated (or copied) into x', then the records of the block's groups 8 wave .. 8 wave + 7 (they
+// read only this block of x').  COHERENT: x is fp32 written by other workgroups of the same
+// launch, read at the device coherence point (no stale cache lines).
+template <int XDT, bool ROT, bool COHERENT = false>
+__device__ __forceinline__ void prep_linear(const void* __restrict__ x, const uint32_t* __restrict__ sign_bits,
+                                            int wave, int lane, uint32_t xb) {
+  float xv[16];
+  if constexpr (COHERENT) {
+    float* xp = const_cast<float*>(static_cast<const float*>(x)) + int64_t(wave) * kBlock + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xv[j] = __hip_atomic_load(xp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    load16<XDT>(x, int64_t(wave) * kBlock + 16 * lane, xv);
+  }
+  uint32_t sw = 0;
+  if constexpr (ROT) sw = sign_bits[wave * 32 + (lane >> 1)] >> ((lane & 1) * 16);
+  const uint32_t xblock = xb + uint32_t(kRotScratch * wave);
+  if constexpr (ROT) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xv[j] = __uint_as_float(__float_as_uint(xv[j]) ^ (((sw >> j) & 1u) << 31));
+    rotate_block(xv, xblock, xblock, lane);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = 16 * lane + j;
+      lds_st<float>(xblock + 4u * uint32_t(kXGroup * (e >> 7) + (e & 127)), xv[j]);
+    }
+  }
+  wave_lds_fence();
+  if (lane < 8 * kSteps) {
+    const int task = 8 * kSteps * wave + lane;
+    const int g = task / kSteps, st = task - kSteps * g;
+    build_record(xb, g, st, uint32_t(kSlot * task + kRecOff));
+  }
+}
+
+// The tile part of one linear, for tile wave cw of the workgroup: the decode table (with_table),
+// the weight loads, barrier C (the records are ready), the matrix loop, barrier D, y.  The
+// workgroup takes tiles [t0, t1) (HALVES waves each); lane group kb of the wave of half h walks
+// groups h G4 / HALVES .. of quarter kb of its tile's 16 rows, and the halves' sums meet in LDS.
+template <int G4, int HALVES, int PD = 0, bool COHERENT = false>
+__device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                                            float* __restrict__ y, int n, int t0, int t1, int cw, int lane,
+                                            uint32_t part_lds, bool with_table, int ctid, int cthreads) {
   constexpr int kGroups = 4 * G4;
-  constexpr int kK = kGroup * kGroups;
   constexpr int kRowBytes = kB3GroupBytes * kGroups;
   constexpr int kLaneBytes = kB3GroupBytes * G4;             // a quarter of a row
   constexpr int kHG = G4 / HALVES;                            // groups of a quarter per wave
   constexpr int kDw = (13 * kHG + 1) / 2;                     // code dwords a wave's lane reads
   constexpr int kChunks = kDw / 16;                           // whole 64-byte chunks of them
   constexpr int kTailLoads = (kDw - 16 * kChunks + 3) / 4;    // 16-byte loads for the rest
-  constexpr int kPrep = kK / kBlock;                          // activation waves
   constexpr int kTotal = kSteps * kHG;                        // matrix steps of a wave
   // operands fetched this many steps ahead of their matrix instruction (fewer when the lane holds
-  // the codes of a whole quarter, to stay within the registers of 16 waves)
-  constexpr int kPD = HALVES > 1 ? 3 : kDw > 40 ? 1 : 2;
-  D1_TS(0);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the codes of a whole quarter, to stay within the registers of 16 waves; PD > 0 overrides)
+  constexpr int kPD = PD > 0 ? PD : HALVES > 1 ? 3 : kDw > 40 ? 1 : 2;
   const int kb = lane >> 4, col = lane & 15;
-  const uint32_t xb = uint32_t(nslots * kSlot);              // x' (fp32, 17 floats per 16)
-  const uint32_t part_lds = xb + uint32_t(kPrep * kRotScratch);  // halves' partial sums
-
-  if (wave < kPrep) {
-    // ---- activation wave: block `wave` of x, rotated (or copied) into x', then the records of
-    // its groups 8 wave .. 8 wave + 7 (they read only this block of x')
-    float xv[16];
-    load16<XDT>(x, int64_t(wave) * kBlock + 16 * lane, xv);
-    uint32_t sw = 0;
-    if constexpr (ROT) sw = sign_bits[wave * 32 + (lane >> 1)] >> ((lane & 1) * 16);
-    D1_TS(1);
-    const uint32_t xblock = xb + uint32_t(kRotScratch * wave);
-    if constexpr (ROT) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xv[j] = __uint_as_float(__float_as_uint(xv[j]) ^ (((sw >> j) & 1u) << 31));
-      rotate_block(xv, xblock, xblock, lane);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int e = 16 * lane + j;
-        lds_st<float>(xblock + 4u * uint32_t(kXGroup * (e >> 7) + (e & 127)), xv[j]);
-      }
-    }
-    wave_lds_fence();
-    D1_TS(2);
-    if (lane < 8 * kSteps) {
-      const int task = 8 * kSteps * wave + lane;
-      const int g = task / kSteps, st = task - kSteps * g;
-      build_record(xb, g, st, uint32_t(kSlot * task + kRecOff));
-    }
-    D1_TS(3);
-    lds_barrier();  // C: records complete
-    lds_barrier();  // D
-    return;
-  }
-
-  // ---- tile wave
-  const int cw = wave - kPrep, h = cw % HALVES;
-  const int t0 = int((int64_t(blockIdx.x) * tiles) / grid);
-  const int t1 = int((int64_t(blockIdx.x + 1) * tiles) / grid);
+  const int h = cw % HALVES;
   const int tile_in_wg = cw / HALVES;
   const bool has_tile = tile_in_wg < t1 - t0;
   const int row = 16 * (t0 + tile_in_wg) + col;
   const int d0w = (13 * h * kHG - ((h * kHG) & 1)) / 2;       // first code dword of this wave's groups
-  // ---- decode table first: the activation waves (launched first) get their loads of x out
-  // ahead of the weight stream; then the decode table (entry e at 256 e, copies at 4 c) and the zero records
-  const int ctid = threadIdx.x - 64 * kPrep, cthreads = nthreads - 64 * kPrep;
-  for (int e = ctid; e < kTableEntries; e += cthreads) {
-    const uint32_t v = trit_nibbles(uint32_t(e));
+  // ---- decode table first (once per launch): the activation waves (launched first) get their
+  // loads of x out ahead of the weight stream; then the decode table (entry e at 256 e, copies at
+  // 4 c) and the zero records
+  if (with_table) {
+    for (int e = ctid; e < kTableEntries; e += cthreads) {
+      const uint32_t v = trit_nibbles(uint32_t(e));
 #pragma unroll
-    for (int part = 0; part < kCopies / 4; ++part) lds_st<u32x4>(uint32_t(e) * kSlot + 16u * part, u32x4{v, v, v, v});
+      for (int part = 0; part < kCopies / 4; ++part) lds_st<u32x4>(uint32_t(e) * kSlot + 16u * part, u32x4{v, v, v, v});
+    }
+    for (int k = ctid; k < kSteps * 8; k += cthreads) {  // records 7 kGroups .. 7 kGroups + 6: zeros
+      const uint32_t a = uint32_t(kSlot * (kSteps * kGroups + (k >> 3)) + kRecOff + 16 * (k & 7));
+      lds_st<u32x4>(a, u32x4{0u, 0u, 0u, 0u});
+    }
   }
-  for (int k = ctid; k < kSteps * 8; k += cthreads) {  // records 7 kGroups .. 7 kGroups + 6: zeros
-    const uint32_t a = uint32_t(kSlot * (kSteps * kGroups + (k >> 3)) + kRecOff + 16 * (k & 7));
-    lds_st<u32x4>(a, u32x4{0u, 0u, 0u, 0u});
-  }
-  D1_TS(1);
   u32x4 R[kChunks > 0 ? kChunks : 1][4];
   u32x4 Tl[kTailLoads > 0 ? kTailLoads : 1];
   uint32_t S[(G4 + 1) / 2];
@@ -387,10 +374,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
 #pragma unroll
     for (int i = 0; i < (G4 + 1) / 2; ++i) S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff + 4u * i, 0, 0);
   }
-  D1_TS(2);
-  D1_TS(3);
   lds_barrier();  // C
-  D1_TS(4);
 
   float acc = 0.f;
   // the wave's half as a compile-time constant, so every register index below is one
@@ -411,7 +395,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
     for (int i = 0; i < kTailLoads; ++i)
 #pragma unroll
       for (int d = 0; d < 4; ++d) W[16 * kChunks + 4 * i + d] = Tl[i][d];
-    D1_TS(5);
 
     const uint32_t copy = uint32_t(4 * (lane & 31));
     // A row col of this lane: limb (col & 3) of lane group (col >> 2)'s record; zero records off
@@ -483,9 +466,158 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
   if (has_tile && h == 0 && lane < 16) {
 #pragma unroll
     for (int hh = 1; hh < HALVES; ++hh) acc += lds_ld<float>(part_lds + 4u * uint32_t(16 * (HALVES * tile_in_wg + hh) + col));
-    if (row < n) y[row] = acc;
+    if (row < n) {
+      if constexpr (COHERENT)  // written through to the device coherence point (read by other XCDs next)
+        __hip_atomic_store(y + row, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        y[row] = acc;
+    }
   }
-  D1_TS(6);
+}
+
+// Kernel.  Waves 0 .. kPrep - 1 prepare the activations (kPrep = K / 1024, one 1024-block each:
+// rotation, then the records of the block's 8 groups); the tile waves follow, HALVES per tile.
+template <int G4, int HALVES, int XDT, bool ROT>
+__global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, const void* __restrict__ x,
+    const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int n, int tiles, int nslots, int grid, int nthreads) {
+  constexpr int kPrep = G4 / 2;                               // K / 1024 activation waves
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t xb = uint32_t(nslots * kSlot);              // x' (fp32, 136 floats per 128-group)
+  const uint32_t part_lds = xb + uint32_t(kPrep * kRotScratch);  // halves' partial sums
+  if (wave < kPrep) {
+    prep_linear<XDT, ROT>(x, sign_bits, wave, lane, xb);
+    lds_barrier();  // C: records complete
+    lds_barrier();  // D
+    return;
+  }
+  // workgroup w takes tiles [w T / G, (w + 1) T / G)
+  const int t0 = int((int64_t(blockIdx.x) * tiles) / grid);
+  const int t1 = int((int64_t(blockIdx.x + 1) * tiles) / grid);
+  tile_linear<G4, HALVES>(packed, scales, y, n, t0, t1, wave - kPrep, lane, part_lds, true,
+                          int(threadIdx.x) - 64 * kPrep, nthreads - 64 * kPrep);
+}
+
+// ---------------------------------------------------------------- chained linears
+// One launch runs linears 0 .. count - 1 in order; linear i + 1 takes the first K outputs of
+// linear i as its activations.  Every workgroup is resident at once (one per compute unit), and
+// between linears each one waits on a device-wide count of the workgroups that have stored their
+// rows of the previous output.  The tile waves issue the next linear's weight loads before that
+// wait (they do not depend on x), so a linear's weight stream overlaps the previous linear's tail
+// and the hand-over, and no launch separates the linears.  (Measured: the hand-over through the
+// count costs more than a kernel boundary in a HIP graph, so separate launches are faster.)
+struct ChainArgs {
+  const uint8_t* packed[TB_CHAIN_MAX];
+  const uint16_t* scales[TB_CHAIN_MAX];
+  float* y[TB_CHAIN_MAX];
+  int n[TB_CHAIN_MAX];
+  const void* x0;
+  const uint32_t* sign_bits;
+  int32_t* sync;  // [0, count): arrivals per linear; [count]: finished workgroups; [count + 1]: status
+  int count, spin_limit, nslots, grid, nthreads;
+};
+
+// Wait until *ctr reaches target, polling at most `limit` times; on time-out set bit 0 of *status
+// and return anyway (the results of the call are then invalid, and the caller sees the status).
+//
+// Hand-over without cache maintenance: the producers write y with device-coherent stores (written
+// through to the coherence point, complete once the store barrier has waited for them) before
+// they bump the count, and the consumers poll the count and then read x with device-coherent loads.
+// So no level of cache holds a stale copy on either side, and the count is only bumped after the
+// data it announces is in place.  (Release/acquire fences at device scope would write back and
+// invalidate each XCD's whole L2 every time: measured at about 50 us per hand-over.)
+__device__ __forceinline__ void wait_count(int32_t* ctr, int target, int limit, int32_t* status, int lane) {
+  for (int it = 0;; ++it) {
+    const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= target) return;
+    if (it >= limit) {
+      if (lane == 0) __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+template <int G4, int XDT0>
+__global__ __launch_bounds__(64 * kMaxWaves) void chain_kernel(ChainArgs a) {
+  constexpr int kPrep = G4 / 2;
+  constexpr int kTilesPerRound = (kMaxWaves - kPrep) / 2;  // two waves (halves of K) per tile
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t xb = uint32_t(a.nslots * kSlot);
+  const uint32_t part_lds = xb + uint32_t(kPrep * kRotScratch);
+  // This workgroup's tiles [t0, t1) of linear i, taken kTilesPerRound at a time.
+  auto tile_range = [&](int n, int& t0, int& t1) {
+    const int tiles = (n + 15) / 16;
+    t0 = int((int64_t(blockIdx.x) * tiles) / a.grid);
+    t1 = int((int64_t(blockIdx.x + 1) * tiles) / a.grid);
+  };
+  auto rounds_of = [&](int t0, int t1) { return max(1, (t1 - t0 + kTilesPerRound - 1) / kTilesPerRound); };
+  // Each role runs its own loop over the linears with the same workgroup barriers (C and D per
+  // round, then the store barrier), so neither role's state is live in the other's code.
+  if (wave < kPrep) {
+    int32_t* status = a.sync + a.count + 1;
+    for (int i = 0; i < a.count; ++i) {
+      // linear i's row count and the previous output, by selects over the unrolled index
+      // (indexing the argument arrays with i would copy them to scratch memory)
+      int n = a.n[0];
+      const float* xprev = a.y[0];
+#pragma unroll
+      for (int j = 1; j < TB_CHAIN_MAX; ++j)
+        if (i == j) {
+          n = a.n[j];
+          xprev = a.y[j - 1];
+        }
+      if (i == 0) {
+        prep_linear<XDT0, true>(a.x0, a.sign_bits, wave, lane, xb);
+      } else {
+        wait_count(a.sync + i - 1, a.grid, a.spin_limit, status, lane);
+        prep_linear<TB_F32, true, true>(xprev, a.sign_bits, wave, lane, xb);
+      }
+      int t0, t1;
+      tile_range(n, t0, t1);
+      for (int r = rounds_of(t0, t1); r > 0; --r) {
+        lds_barrier();  // C
+        lds_barrier();  // D
+      }
+      // every wave's device-coherent stores of y_i are complete (the barrier waits for them): count
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the last workgroup to finish (no workgroup waits any more) clears the counts for the next call
+    if (threadIdx.x == 0) {
+      const int prev = __hip_atomic_fetch_add(a.sync + a.count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == a.grid - 1)
+        for (int i = 0; i <= a.count; ++i) __hip_atomic_store(a.sync + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  for (int i = 0; i < a.count; ++i) {
+    const uint8_t* packed = a.packed[0];
+    const uint16_t* scales = a.scales[0];
+    float* y = a.y[0];
+    int n = a.n[0];
+#pragma unroll
+    for (int j = 1; j < TB_CHAIN_MAX; ++j)
+      if (i == j) {
+        packed = a.packed[j];
+        scales = a.scales[j];
+        y = a.y[j];
+        n = a.n[j];
+      }
+    int t0, t1;
+    tile_range(n, t0, t1);
+    const int rounds = rounds_of(t0, t1);
+    for (int r = 0; r < rounds; ++r) {
+      // the lane index made opaque per round, so the lane-dependent set-up is not hoisted out of
+      // the loops (it would stay live across them and spill)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int u0 = t0 + r * kTilesPerRound, u1 = min(t1, u0 + kTilesPerRound);
+      tile_linear<G4, 2, 2, true>(packed, scales, y, n, u0, u1, wave - kPrep, ln, part_lds, i == 0 && r == 0,
+                                  64 * (wave - kPrep) + ln, a.nthreads - 64 * kPrep);
+    }
+    __syncthreads();  // this wave's rows of y_i are stored
+  }
 }
 
 int cu_count() {
@@ -558,6 +690,69 @@ bool decode1_supports(int packing, int b, int n, int k) {
   int grid, per_wg;
   plan(n, grid, per_wg);
   return k / kBlock + per_wg <= kMaxWaves;
+}
+
+namespace {
+
+template <int G4, int XDT0>
+void run_chain(ChainArgs& a, int nw, hipStream_t s) {
+  constexpr int kGroups = 4 * G4;
+  a.nslots = max(kTableEntries, kSteps * kGroups + kSteps);
+  const size_t lds = size_t(a.nslots) * kSlot + size_t(G4 / 2) * kRotScratch + size_t(64) * kMaxWaves;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<G4, XDT0>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  a.nthreads = 64 * nw;
+  chain_kernel<G4, XDT0><<<a.grid, 64 * nw, lds, s>>>(a);
+}
+
+template <int XDT0>
+void chain_k(int k, ChainArgs& a, int nw, hipStream_t s) {
+  switch (k) {
+    case 1024: run_chain<2, XDT0>(a, nw, s); break;
+    case 2048: run_chain<4, XDT0>(a, nw, s); break;
+    case 3072: run_chain<6, XDT0>(a, nw, s); break;
+    case 4096: run_chain<8, XDT0>(a, nw, s); break;
+    default: run_chain<10, XDT0>(a, nw, s); break;
+  }
+}
+
+}  // namespace
+
+// The chained launch's plan: one workgroup per compute unit, two waves per tile (halves of K),
+// at most (16 - K/1024) / 2 tiles at a time (more run in rounds).  Returns the waves per workgroup.
+int chain_plan(const int64_t* n, int count, int k) {
+  const int grid = cu_count(), prep = k / kBlock, per_round = (kMaxWaves - prep) / 2;
+  int tiles_wg = 1;
+  for (int i = 0; i < count; ++i) tiles_wg = max(tiles_wg, int(((n[i] + 15) / 16 + grid - 1) / grid));
+  return prep + 2 * min(tiles_wg, per_round);
+}
+
+bool launch_chain(const tb_chain_linear* lin, int count, const void* x0, int x_dt, const uint32_t* sign_bits, int k,
+                  int32_t* sync, int spin_limit, hipStream_t s) {
+  if (count < 1 || count > TB_CHAIN_MAX || k % kBlock != 0 || k < kBlock || k > 5120) return false;
+  int64_t n[TB_CHAIN_MAX];
+  for (int i = 0; i < count; ++i) n[i] = lin[i].N;
+  const int nw = chain_plan(n, count, k);
+  ChainArgs a{};
+  for (int i = 0; i < count; ++i) {
+    a.packed[i] = lin[i].packed;
+    a.scales[i] = lin[i].scales;
+    a.y[i] = lin[i].y;
+    a.n[i] = int(lin[i].N);
+  }
+  a.x0 = x0;
+  a.sign_bits = sign_bits;
+  a.sync = sync;
+  a.count = count;
+  a.spin_limit = spin_limit;
+  a.grid = cu_count();
+  if (x_dt == TB_F32) chain_k<TB_F32>(k, a, nw, s);
+  else if (x_dt == TB_F16) chain_k<TB_F16>(k, a, nw, s);
+  else chain_k<TB_BF16>(k, a, nw, s);
+  return true;
 }
 
 bool launch_decode1(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,

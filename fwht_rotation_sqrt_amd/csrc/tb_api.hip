@@ -177,6 +177,30 @@ int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales
   return tb_linear_ws(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, scratch, need, stream);
 }
 
+int tb_decode_chain(int packing, const tb_chain_linear* linears, int count, const void* x0, int x_dtype,
+                    const uint32_t* sign_bits, int64_t K, int32_t* sync, int64_t sync_words, int spin_limit,
+                    void* stream) {
+  if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;
+  if (count < 1 || count > TB_CHAIN_MAX || K <= 0 || K % tb::kBlock != 0) return TB_ERR_SHAPE;
+  if (!linears) return TB_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    const int64_t n = linears[i].N;
+    if (n < 1 || !fits(n, K) || (i + 1 < count && n < K)) return TB_ERR_SHAPE;
+    if (!linears[i].packed || !linears[i].scales || !linears[i].y) return TB_ERR_NULL;
+    if (!aligned16(linears[i].packed) || !aligned16(linears[i].scales) || !aligned16(linears[i].y))
+      return TB_ERR_ALIGN;
+  }
+  if (x_dtype != TB_F32 && x_dtype != TB_F16 && x_dtype != TB_BF16) return TB_ERR_DTYPE;
+  if (!x0 || !sign_bits || !sync) return TB_ERR_NULL;
+  if (!aligned16(x0) || !aligned16(sign_bits) || !aligned16(sync)) return TB_ERR_ALIGN;
+  if (sync_words < count + 2) return TB_ERR_WORKSPACE;
+  if (packing != TB_PACK_BASE3 || K > 5120) return TB_ERR_UNSUPPORTED;
+  if (!tb::launch_chain(linears, count, x0, x_dtype, sign_bits, int(K), sync, spin_limit > 0 ? spin_limit : 1 << 22,
+                        static_cast<hipStream_t>(stream)))
+    return TB_ERR_UNSUPPORTED;
+  return finish_launch();
+}
+
 int tb_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr_f16,
             float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (packing != TB_PACK_2BIT && packing != TB_PACK_BASE3) return TB_ERR_UNSUPPORTED;

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "tb.h"
 #include <stdint.h>
 
 namespace tb {
@@ -52,6 +54,10 @@ void launch_stream_read(const uint8_t* src, int64_t bytes, uint32_t* sink, hipSt
 bool decode1_supports(int packing, int b, int n, int k);
 bool launch_decode1(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                     const uint32_t* sign_bits, bool rotate, float* y, int n, int k, hipStream_t s);
+// Chained batch-1 base-3 linears in one launch (decode1.hip): false when the chain is not supported
+// (count, K, or too many tiles per workgroup for a linear).
+bool launch_chain(const tb_chain_linear* lin, int count, const void* x0, int x_dt, const uint32_t* sign_bits, int k,
+                  int32_t* sync, int spin_limit, hipStream_t s);
 
 // Walsh-Hadamard butterflies across lane bits 4 and 5 of a wave (partner
 // lane l ^ 16, then l ^ 32), for 16 values per lane: the lane whose bit is 0

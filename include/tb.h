@@ -184,6 +184,50 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
 int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
                       const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream);
 
+/* Persistent multi-linear decode: up to TB_CHAIN_MAX dependent batch-1 linears
+ * in ONE launch.  Linear 0 computes y_0 = W_0 (R_K x0); linear i > 0 computes
+ * y_i = W_i (R_K y_{i-1}[0 .. K)), i.e. it takes the first K outputs of the
+ * previous linear as its (unrotated, fp32) activations.  Between linears every
+ * workgroup waits on a device-side count of the workgroups that have stored
+ * their rows of the previous output; the weight loads of the next linear are
+ * issued before that wait (weights do not depend on x), so no launch separates
+ * the linears and the next weight stream overlaps the previous one's tail.
+ * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
+ * reach 1.76 bit" (f(x) = W(Rx), g128 scales) and "Throughput" (decode reads
+ * every weight byte once per token; tg128 is a chain of such products).
+ * packing: TB_PACK_BASE3 only (else TB_ERR_UNSUPPORTED).  linears: HOST array
+ * of count (1..TB_CHAIN_MAX) descriptors {packed [N][26 K/128], scales fp16
+ * [N][K/128], y fp32 [N], N}, read during the call; N_i >= K for every linear
+ * but the last (else TB_ERR_SHAPE).  x0: [K] of x_dtype; sign_bits: uint32
+ * [K/32], the same R_K for every linear.  K a multiple of 1024 up to 5120
+ * (else TB_ERR_UNSUPPORTED), and at most 16 - K/1024 row tiles of 16 per
+ * compute unit for any linear (about 176 x the compute units rows at K = 5120;
+ * else TB_ERR_UNSUPPORTED).
+ * sync: device int32 [sync_words >= count + 2], all zero before the first call
+ * (the caller clears it once); a call that completes leaves its counts zero for
+ * the next call on the same stream.  Word count + 1 is the status: bit 0 is
+ * set when a wait polled spin_limit times without the count arriving (spin_limit
+ * <= 0: 2^22 polls, about 0.1-1 s); every wait is bounded, the launch always
+ * ends, but its outputs are then invalid and the caller must clear sync again.
+ * The launch needs every one of its workgroups (one per compute unit) resident
+ * at once, so it should not share the GPU with other work.  Calls sharing a
+ * sync buffer must be ordered (one stream).
+ * Measured on MI355X it is SLOWER than one tb_linear launch per linear in a
+ * HIP graph (q/k/v -> o: 33 us against 16 us): a device-wide hand-over costs
+ * about 10 us of atomics and polling, a kernel boundary in a graph about 1-2 us,
+ * and even with no hand-over at all the chained launch does not beat separate
+ * ones.  Prefer tb_linear (or tb_linear_ws) under a HIP graph for decode. */
+#define TB_CHAIN_MAX 8
+typedef struct tb_chain_linear {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  float* y;
+  int64_t N;
+} tb_chain_linear;
+int tb_decode_chain(int packing, const tb_chain_linear* linears, int count, const void* x0, int x_dtype,
+                    const uint32_t* sign_bits, int64_t K, int32_t* sync, int64_t sync_words, int spin_limit,
+                    void* stream);
+
 /* Prefill product Y = X' W_hat^T for many rows: Y[m][n] = sum_k X'[m][k] s[n][k/128] t[n][k].
  * Pages: "Ternary Bonsai 2 27B release", sections "How the ternary weights
  * reach 1.76 bit" and "Throughput" (pp512 prompt processing).

@@ -175,6 +175,37 @@ def test_linear_noalloc_validation():
     assert g(1, P, P, P, 2, None, P, 1, 8, 1024, None) == NULL
 
 
+def test_decode_chain_validation():
+    lib = tb.library()
+    g = lib.tb_decode_chain
+    Lin = tb.ChainLinear
+
+    def arr(*ns, p=P):
+        a = (Lin * len(ns))()
+        for i, n in enumerate(ns):
+            a[i] = Lin(p, p, p, n)
+        return a
+
+    two = arr(2048, 512)
+    # (packing, linears, count, x0, x_dtype, sign_bits, K, sync, sync_words, spin_limit, stream)
+    assert g(3, two, 2, P, 2, P, 1024, P, 4, 0, None) == UNSUP
+    assert g(1, two, 0, P, 2, P, 1024, P, 4, 0, None) == SHAPE
+    assert g(1, two, tb.TB_CHAIN_MAX + 1, P, 2, P, 1024, P, 4, 0, None) == SHAPE
+    assert g(1, two, 2, P, 2, P, 1000, P, 4, 0, None) == SHAPE              # K % 1024 != 0
+    assert g(1, arr(512, 2048), 2, P, 2, P, 1024, P, 4, 0, None) == SHAPE   # an inner N below K
+    assert g(1, arr(0), 1, P, 2, P, 1024, P, 3, 0, None) == SHAPE
+    assert g(1, None, 2, P, 2, P, 1024, P, 4, 0, None) == NULL
+    assert g(1, arr(2048, 512, p=0), 2, P, 2, P, 1024, P, 4, 0, None) == NULL
+    assert g(1, arr(2048, 512, p=MIS), 2, P, 2, P, 1024, P, 4, 0, None) == ALIGN
+    assert g(1, two, 2, P, 3, P, 1024, P, 4, 0, None) == DTYPE
+    assert g(1, two, 2, None, 2, P, 1024, P, 4, 0, None) == NULL
+    assert g(1, two, 2, P, 2, P, 1024, None, 4, 0, None) == NULL
+    assert g(1, two, 2, P, 2, MIS, 1024, P, 4, 0, None) == ALIGN
+    assert g(1, two, 2, P, 2, P, 1024, P, 3, 0, None) == 7                  # sync needs count + 2 words
+    assert g(0, two, 2, P, 2, P, 1024, P, 4, 0, None) == UNSUP              # 2-bit codes
+    assert g(1, arr(8192, 512), 2, P, 2, P, 6144, P, 4, 0, None) == UNSUP   # K > 5120
+
+
 def test_ternarize_validation():
     lib = tb.library()
     g = lib.tb_ternarize
