@@ -112,7 +112,10 @@ __device__ __forceinline__ void a_issue(ARaw<XF32>& r, __amdgpu_buffer_rsrc_t xr
 
 // The exponent e of the (activation row, group) scale: the largest |x'| of the row's 128 values
 // (this lane's 32 and those of the lanes l ^ 16, l ^ 32, l ^ 48, which hold the row's other
-// quarters) times 2^-e lies in [2^14, 2^15).  All four lanes get the same e; 0 for an all-zero group.
+// quarters) times 2^-e lies in [2^14, 2^15).  All four lanes get the same e.  e = 0 (no scale)
+// for an all-zero group and for a largest value in [2^-6, 2^15): there the unscaled split already
+// carries every value to 2^-18 of the largest (the fp16 subnormal floor is 2^-24), so typical
+// activations skip the scaling work.
 __device__ __forceinline__ int a_exponent(const ARaw<1>& r) {
   uint32_t m = 0;
 #pragma unroll
@@ -123,12 +126,12 @@ __device__ __forceinline__ int a_exponent(const ARaw<1>& r) {
   m = max(uint32_t(p[0]), uint32_t(p[1]));
   p = __builtin_amdgcn_permlane32_swap(m, m, false, false);
   m = max(uint32_t(p[0]), uint32_t(p[1]));
-  if (m == 0) return 0;
+  if (m == 0 || (m >= 0x3C800000u && m < 0x47000000u)) return 0;   // 0, or 2^-6 <= max < 2^15
   const int ef = int(m >> 23);                 // an fp32 subnormal maximum counts as exponent -126
   return (ef > 0 ? ef : 1) - 127 - 14;
 }
 
-template <int XF32>
+template <int XF32, bool SCALED>
 __device__ __forceinline__ void a_operands(const ARaw<XF32>& r, int e, u32x4 (&hi)[4], u32x4 (&lo)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -138,9 +141,11 @@ __device__ __forceinline__ void a_operands(const ARaw<XF32>& r, int e, u32x4 (&h
       if constexpr (XF32) {
         // scaled by 2^-e (exact unless far below the group's largest value); hi: cut to fp16
         // precision (exact in fp16 for 2^-14 <= |x| < 65520); lo: the exact rest, rounded to fp16
-        const uint32_t u0 = __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(r.v[a >> 2][a & 3]), -e));
-        const uint32_t u1 =
-            __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(r.v[(a + 8) >> 2][(a + 8) & 3]), -e));
+        uint32_t u0 = r.v[a >> 2][a & 3], u1 = r.v[(a + 8) >> 2][(a + 8) & 3];
+        if constexpr (SCALED) {
+          u0 = __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(u0), -e));
+          u1 = __float_as_uint(__builtin_amdgcn_ldexpf(__uint_as_float(u1), -e));
+        }
         const float h0 = __uint_as_float(u0 & 0xFFFFE000u), h1 = __uint_as_float(u1 & 0xFFFFE000u);
         hi[j][p] = pack_f16(h0, h1);
         lo[j][p] = pack_f16(__uint_as_float(u0) - h0, __uint_as_float(u1) - h1);
@@ -292,15 +297,21 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
     u32x4 ahi[MB][4], alo[MB][4];
     floatx4 neg_sum[MB];
     int eo[MB][4];
+    bool scaled = false;  // wave-uniform: some row of the group needs its scale
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       int e = 0;
       if constexpr (XF32) {
         e = a_exponent(ac[mb]);
+        const bool sc_mb = __builtin_amdgcn_ballot_w64(e != 0) != 0;
+        scaled = scaled || sc_mb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) eo[mb][i] = __shfl(e, 4 * q + i);
+        for (int i = 0; i < 4; ++i) eo[mb][i] = sc_mb ? __shfl(e, 4 * q + i) : 0;
+        if (sc_mb) a_operands<XF32, true>(ac[mb], e, ahi[mb], alo[mb]);
+        else a_operands<XF32, false>(ac[mb], 0, ahi[mb], alo[mb]);
+      } else {
+        a_operands<XF32, false>(ac[mb], 0, ahi[mb], alo[mb]);
       }
-      a_operands<XF32>(ac[mb], e, ahi[mb], alo[mb]);
       neg_sum[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -329,13 +340,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
           if constexpr (XF32) part[mb] = mfma(alo[mb][j], b[j], part[mb]);
         }
       const float s = 16384.f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sbits)));
+      if (XF32 && scaled) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = XF32 ? __builtin_amdgcn_ldexpf(part[mb][i], eo[mb][i]) : part[mb][i];
-          acc[t][mb][i] = fmaf(s, pv, acc[t][mb][i]);
-        }
+          for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(s, __builtin_amdgcn_ldexpf(part[mb][i], eo[mb][i]), acc[t][mb][i]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(s, part[mb][i], acc[t][mb][i]);
+      }
     }
   }
 
