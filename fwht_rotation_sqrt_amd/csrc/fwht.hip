@@ -71,6 +71,15 @@ __device__ __forceinline__ void store16(void* base, int64_t off, const float v[1
   }
 }
 
+// Each wave transposes through its own LDS region, so a wave-level LDS fence orders the
+// transposes (a workgroup barrier would also wait for the other waves and for this wave's
+// outstanding global memory operations).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Butterflies over register index bits: pairs (j, j + h) for h = 1, 2, 4, 8.
 __device__ __forceinline__ void butterfly16(float v[16]) {
 #pragma unroll
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(64 * kWaves) void fwht1024_kernel(const void* x, vo
   const int lane = threadIdx.x & 63;
   const int64_t blk = int64_t(blockIdx.x) * kWaves + wave;
   const bool active = blk < nblocks;
-  const int64_t b = active ? blk : 0;  // idle waves still join the barriers
+  const int64_t b = active ? blk : 0;  // idle waves compute on block 0 and store nothing
   const int beta = int(b % blocks_per_row);
   const int64_t off = b * kBlock + 16 * lane;
   float* L = lds[wave];
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(64 * kWaves) void fwht1024_kernel(const void* x, vo
   // element i lives at L[i + i/16]; layout A: i = 16*lane + j
 #pragma unroll
   for (int j = 0; j < 16; ++j) L[17 * lane + j] = v[j];
-  __syncthreads();
+  wave_lds_sync();
   // layout B: i = (lane & 15) + 16*j + 256*(lane >> 4)
   const int bidx = (lane & 15) + 272 * (lane >> 4);
 #pragma unroll
@@ -121,10 +130,10 @@ __global__ __launch_bounds__(64 * kWaves) void fwht1024_kernel(const void* x, vo
 
   butterfly_lane_bits_4_5(v, lane);  // index bits 8, 9 are lane bits 4, 5
 
-  __syncthreads();
+  wave_lds_sync();
 #pragma unroll
   for (int j = 0; j < 16; ++j) L[bidx + 17 * j] = v[j];
-  __syncthreads();
+  wave_lds_sync();
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = L[17 * lane + j] * 0.03125f;
 
