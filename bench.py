@@ -234,6 +234,21 @@ def host_threads():
     return max(1, min(n, int(env))) if env and env.isdigit() else n
 
 
+def rotate_k17408_us(steps=200):
+    """tb_fwht_rotate of one bf16 row of K = 17408 (17 blocks) to fp32, us per call."""
+    k = synth.FFN
+    x = dev(synth.activations(synth.rng(1, synth.T_X, 0, 9), 1, k, dtype="bf16").view(np.int16)).view(torch.bfloat16)
+    sg = dev(synth.sign_bits(synth.rng(1, synth.T_SIGNS, 0, 9), k).view(np.int32))
+    xr = torch.empty((1, k), dtype=torch.float32, device="cuda")
+
+    def rot():
+        for _ in range(steps):
+            tb.tb_fwht_rotate(x, sg, out=xr)
+
+    _, g = time_graph(rot, rot)
+    return event_time(g) / steps * 1e6
+
+
 def cpu_baseline(d, budget_s=(8.0, 5.0)):
     """The plain C++ oracle (fp64 loops) on the same decode step, rotate + product over all
     17408 rows: single-threaded, then with its output rows split over every host thread."""
@@ -255,10 +270,21 @@ def cpu_baseline(d, budget_s=(8.0, 5.0)):
     cores = host_threads()
     v1, r1, e1 = out[1]
     vn, rn, en = out[cores]
+    # the same oracle as a prefill product on a sample of pp512's rows (x' already rotated),
+    # all threads: multiply-adds per second (2 flops each)
+    rows = 16
+    xs = synth.bf16_bits_to_f64(synth.activations(synth.rng(3, synth.T_X), rows, k, dtype="bf16"))
+    t0 = time.perf_counter()
+    cpp_oracle.linear("base3", packed, li.scales, xs, None, cores)
+    eg = time.perf_counter() - t0
+    gflops = 2.0 * rows * packed.shape[0] * k / eg / 1e9
     return {"value": round(vn, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "single_thread_value": round(v1, 5), "cpu_model": cpu_model(),
+            "gemm_sample_gflops": round(gflops, 3),
             "sample": f"plain C++ fp64 oracle, rotate + product of the full 17408x5120 base-3 step at batch 1: "
-                      f"{rn} passes in {en:.1f} s on {cores} threads, {r1} passes in {e1:.1f} s on one"}
+                      f"{rn} passes in {en:.1f} s on {cores} threads, {r1} passes in {e1:.1f} s on one; "
+                      f"gemm_sample_gflops: {rows} rows of the pp512 product (17408x5120 base-3) on {cores} "
+                      f"threads, {eg:.1f} s"}
 
 
 def stream_ceiling(per_copy, reps=20):
@@ -679,6 +705,7 @@ def main():
         "stream_ceiling": stream,
         "sclk_during_decode": sclk,
         "separate_route_us": {"tb_fwht_rotate_b1_k5120": round(t_rot * 1e6, 3),
+                              "tb_fwht_rotate_b1_k17408": round(rotate_k17408_us(), 3),
                               "tb_gemv_base3_17408x5120_b1": round(t_gemv * 1e6, 3)},
         "tokens_per_s_equiv_this_linear": round(1.0 / (wall / args.steps), 1),
         "cpu_baseline": cpu,
@@ -687,6 +714,8 @@ def main():
         rec["pp512_gemm"] = {"tflops": round(gemm["tflops"], 2), "us": round(gemm["us"], 2),
                              "frac_of_fp16_mfma_peak": round(gemm["frac"], 4), "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
                              "rotate_us_512x5120_to_f16": round(gemm["rotate_us"], 2),
+                             # bf16 in + fp16 out, 512 x 5120 x 2 B each
+                             "rotate_gbs_512x5120": round(2 * 512 * 5120 * 2 / (gemm["rotate_us"] * 1e-6) / 1e9, 1),
                              "tokens_per_s_equiv": round(gemm["tokens_per_s"], 1)}
     if gemm3:
         rec["pp512_gemm_base3"] = {"tflops": round(gemm3["tflops"], 2), "us": round(gemm3["us"], 2),

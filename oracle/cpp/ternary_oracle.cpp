@@ -1,4 +1,5 @@
-// Plain C++ reference for y = W(Rx) on packed ternary weights (test infrastructure only).
+// Plain C++ reference for y = W(Rx) on packed ternary weights, and for the two packings
+// (test infrastructure only).
 //
 // Only the tests and the benchmark's CPU-baseline leg load this library.  It is
 // a slow, literal transcription of the same definitions as the numpy oracle
@@ -94,6 +95,76 @@ void product_rows(int packing, const uint8_t* packed, const uint16_t* scales, co
 }  // namespace
 
 extern "C" {
+
+// Trits int8 [n][k] -> packed bytes.  2-bit: byte j = sum_{i<4} (t_{4j+i} + 1) << 2i.  Base-3,
+// per 128-group: 26 bytes, byte j = sum_{i<5} (t_{5j+i} + 1) 3^i over the group extended by two
+// trits of 0.  A trit outside {-1, 0, 1} counts once and is packed as 0.  Returns the count, or
+// -1 on bad sizes.
+int64_t oracle_pack(int packing, const int8_t* trits, int64_t n, int64_t k, uint8_t* packed) {
+  if ((packing != 0 && packing != 1) || n < 0 || k <= 0 || k % 128 != 0) return -1;
+  int64_t bad = 0;
+  auto trit = [&](int64_t r, int64_t i) -> int {
+    const int t = trits[r * k + i];
+    if (t < -1 || t > 1) {
+      ++bad;
+      return 0;
+    }
+    return t;
+  };
+  for (int64_t r = 0; r < n; ++r) {
+    if (packing == 0) {
+      for (int64_t j = 0; j < k / 4; ++j) {
+        int byte = 0;
+        for (int i = 0; i < 4; ++i) byte |= (trit(r, 4 * j + i) + 1) << (2 * i);
+        packed[r * (k / 4) + j] = uint8_t(byte);
+      }
+    } else {
+      for (int64_t g = 0; g < k / 128; ++g)
+        for (int j = 0; j < 26; ++j) {
+          int byte = 0, pow3 = 1;
+          for (int i = 0; i < 5; ++i, pow3 *= 3) {
+            const int e = 5 * j + i;  // element of the extended group
+            byte += (e < 128 ? trit(r, 128 * g + e) + 1 : 1) * pow3;
+          }
+          packed[r * 26 * (k / 128) + 26 * g + j] = uint8_t(byte);
+        }
+    }
+  }
+  return bad;
+}
+
+// Packed bytes -> trits int8 [n][k].  2-bit: code 11 counts once and decodes as 0.  Base-3:
+// trit i of byte b is (b / 3^i) mod 3 - 1; a byte >= 243 counts once and its trits decode as 0; a
+// valid last byte of a group whose two pad digits are not 1 counts once.  Returns the count, or
+// -1 on bad sizes.
+int64_t oracle_unpack(int packing, const uint8_t* packed, int64_t n, int64_t k, int8_t* trits) {
+  if ((packing != 0 && packing != 1) || n < 0 || k <= 0 || k % 128 != 0) return -1;
+  int64_t bad = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    if (packing == 0) {
+      for (int64_t i = 0; i < k; ++i) {
+        const int c = (packed[r * (k / 4) + i / 4] >> (2 * (i % 4))) & 3;
+        if (c == 3) ++bad;
+        trits[r * k + i] = int8_t(c == 3 ? 0 : c - 1);
+      }
+    } else {
+      for (int64_t g = 0; g < k / 128; ++g)
+        for (int j = 0; j < 26; ++j) {
+          const int b = packed[r * 26 * (k / 128) + 26 * g + j];
+          if (b >= 243) ++bad;
+          else if (j == 25 && ((b / 27) % 3 != 1 || (b / 81) % 3 != 1)) ++bad;  // pad digits 3, 4 not 1
+          int rest = b;
+          for (int i = 0; i < 5; ++i) {
+            const int digit = rest % 3;
+            rest /= 3;
+            const int e = 5 * j + i;
+            if (e < 128) trits[r * k + 128 * g + e] = int8_t(b >= 243 ? 0 : digit - 1);
+          }
+        }
+    }
+  }
+  return bad;
+}
 
 // y[b][n] = sum_g s[n][g] sum_{k in g} t[n][k] (R_K x[b])[k], all in float64.
 // x: float64 [B][K] unrotated; sign_bits NULL means x is already rotated.

@@ -12,7 +12,7 @@ import os
 
 import numpy as np
 
-from .cpp_build import LIB, build
+from .cpp_build import LIB, SRC, build
 
 _lib = None
 
@@ -20,12 +20,15 @@ _lib = None
 def library() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build()
+        if not os.path.exists(LIB) or os.path.getmtime(SRC) > os.path.getmtime(LIB):
+            build()  # missing, or older than its source
         lib = ctypes.CDLL(LIB)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.oracle_linear.restype = ctypes.c_int
         lib.oracle_linear.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_int]
+        for name in ("oracle_pack", "oracle_unpack"):
+            getattr(lib, name).restype = i64
+            getattr(lib, name).argtypes = [ctypes.c_int, vp, i64, i64, vp]
         _lib = lib
     return _lib
 
@@ -46,3 +49,25 @@ def linear(packing: str, packed: np.ndarray, scales_bits: np.ndarray, x: np.ndar
     if st != 0:
         raise ValueError(f"oracle_linear rejected the sizes (B={b}, N={n}, K={k})")
     return y
+
+
+def pack(packing: str, trits: np.ndarray):
+    """int8 [N][K] trits -> (uint8 packed [N][row bytes], invalid-trit count)."""
+    t = np.ascontiguousarray(trits, dtype=np.int8)
+    n, k = t.shape
+    out = np.empty((n, k // 4 if packing == "2bit" else 26 * (k // 128)), dtype=np.uint8)
+    bad = library().oracle_pack(0 if packing == "2bit" else 1, t.ctypes.data, n, k, out.ctypes.data)
+    if bad < 0:
+        raise ValueError(f"oracle_pack rejected the sizes (N={n}, K={k})")
+    return out, int(bad)
+
+
+def unpack(packing: str, packed: np.ndarray, k: int):
+    """uint8 packed [N][row bytes] -> (int8 trits [N][K], invalid-code count)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    n = p.shape[0]
+    out = np.empty((n, k), dtype=np.int8)
+    bad = library().oracle_unpack(0 if packing == "2bit" else 1, p.ctypes.data, n, k, out.ctypes.data)
+    if bad < 0:
+        raise ValueError(f"oracle_unpack rejected the sizes (N={n}, K={k})")
+    return out, int(bad)

@@ -49,3 +49,27 @@ def test_cpp_oracle_rejects_bad_sizes():
     with pytest.raises(ValueError):
         cpp_oracle.linear("base3", np.zeros((2, 26), np.uint8), np.zeros((2, 1), np.uint16), np.zeros((1, 128)),
                           np.zeros(4, np.uint32))      # K = 128 cannot be rotated by 1024-blocks
+
+
+@pytest.mark.parametrize("packing", ["2bit", "base3"])
+def test_cpp_pack_unpack_match_numpy_oracle(packing):
+    """The C++ packings against the pinned numpy ones, invalid inputs included: trits outside
+    {-1, 0, 1}; 2-bit code 11; base-3 bytes >= 243 and last bytes with pad digits other than 1."""
+    g = synth.rng(282, 0, 0, 0)
+    t = synth.trits(g, 7, 1024)
+    t[1, 5] = 3
+    t[4, 700] = -2
+    want, bad = (oracle.pack_2bit if packing == "2bit" else oracle.pack_base3)(t)
+    got, gbad = cpp_oracle.pack(packing, t)
+    assert np.array_equal(got, want) and gbad == bad == 2
+    p = want.copy()
+    if packing == "2bit":
+        p[0, 3] |= 0xC0            # one code 11
+        p[6, 200] = 0xFF           # four codes 11
+    else:
+        p[0, 3] = 250              # not a code
+        p[2, 25] = 108 + 81        # last byte of group 0: pad digit 4 = 2
+        p[5, 26 + 25] = 134 - 27   # last byte of group 1: pad digit 3 = 0
+    want_t, want_bad = (oracle.unpack_2bit if packing == "2bit" else oracle.unpack_base3)(p, 1024)
+    got_t, got_bad = cpp_oracle.unpack(packing, p, 1024)
+    assert np.array_equal(got_t, want_t) and got_bad == want_bad and want_bad >= 3
