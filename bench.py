@@ -411,12 +411,18 @@ def suite_token(gen, layers=64, reps=10, per_call=True):
     xr = {H: torch.empty((1, H), dtype=torch.float32, device="cuda"),
           F: torch.empty((1, F), dtype=torch.float32, device="cuda")}
     ys = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n, _ in shapes]
+    # one workspace for every call (down's rows of K = 17408 take it for their partial sums)
+    ws = torch.empty(max(16, max(tb.tb_linear_workspace_bytes("base3", 1, n, k) for _, n, k in shapes)),
+                     dtype=torch.uint8, device="cuda")
+
+    def lin(p, s, x, signs, y):
+        tb.tb_linear_ws("base3", p, s, x, signs, workspace=ws, y=y)
 
     def fused(only=None):
         for lw in W:
             for j, ((_, n, k), (p, s, x)) in enumerate(zip(shapes, lw)):
                 if only is None or only == j:
-                    tb.tb_linear("base3", p, s, x, sg[k], y=ys[j])
+                    lin(p, s, x, sg[k], ys[j])
 
     def separate(rot=True, prod=True):
         for lw in W:
@@ -440,20 +446,21 @@ def suite_token(gen, layers=64, reps=10, per_call=True):
     def dependent():
         x = x_first
         for (pq, sq, _), (po, so, _), (pg, sgg, _), (pd, sd, _) in W:
-            tb.tb_linear("base3", pq, sq, x, sg[H], y=yq)
-            tb.tb_linear("base3", po, so, yq[:, :H], sg[H], y=yo)
-            tb.tb_linear("base3", pg, sgg, yo, sg[H], y=yg)
-            tb.tb_linear("base3", pd, sd, yg[:, :F], sg[F], y=yd)
+            lin(pq, sq, x, sg[H], yq)
+            lin(po, so, yq[:, :H], sg[H], yo)
+            lin(pg, sgg, yo, sg[H], yg)
+            lin(pd, sd, yg[:, :F], sg[F], yd)
             x = yd
 
     def chained():
         x = x_first
         for (pq, sq, _), (po, so, _), (pg, sgg, _), (pd, sd, _) in W:
             tb.tb_decode_chain("base3", [(pq, sq), (po, so), (pg, sgg)], x, sg[H], sync, ys=[yq[0], yo[0], yg[0]])
-            tb.tb_linear("base3", pd, sd, yg[:, :F], sg[F], y=yd)
+            lin(pd, sd, yg[:, :F], sg[F], yd)
             x = yd
 
-    res = {"bytes": total, "layers": layers, "calls_fused": 4 * layers}
+    res = {"bytes": total, "layers": layers, "calls_fused": 4 * layers,
+           "launches_fused": 5 * layers}  # down: the parts' launch and the sum of their partial sums
     for name, fn in (("fused", fused), ("separate", separate),
                      ("rotate_only", lambda: separate(True, False)), ("gemv_only", lambda: separate(False, True)),
                      ("dependent", dependent), ("chained", chained)):
@@ -552,12 +559,18 @@ def run_suite(path, argv):
     lines.append("")
     lines.append("## Block linears (q/k/v/o 5120x5120, gate/up 17408x5120, down 5120x17408)")
     lines.append("")
-    lines.append("| linear | N x K | packing | batch | MB | tb_linear us | GB/s | % peak | rotate us | tb_gemv us |")
-    lines.append("|---|---|---|---|---|---|---|---|---|---|")
+    lines.append("tb_linear_ws differs from tb_linear at batch 8 (one pass over the weights) and for base-3 down "
+                 "at batch 1 (four parts of K on separate workgroups, then a sum of the partial sums).")
+    lines.append("")
+    lines.append("| linear | N x K | packing | batch | MB | tb_linear us | GB/s | % peak | tb_linear_ws us | GB/s (ws) | "
+                 "rotate us | tb_gemv us |")
+    lines.append("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for lin, packing, b, r in rows:
         gbs = r["bytes"] / (r["fused"] * 1e-6) / 1e9
+        gws = r["bytes"] / (r["ws"] * 1e-6) / 1e9
         lines.append(f"| {lin.name} | {lin.n}x{lin.k} | {packing} | {b} | {r['bytes'] / 1e6:.2f} | {r['fused']:.2f} | "
-                     f"{gbs:.0f} | {100 * gbs / pk:.1f} | {r['rotate']:.2f} | {r['gemv']:.2f} |")
+                     f"{gbs:.0f} | {100 * gbs / pk:.1f} | {r['ws']:.2f} | {gws:.0f} | {r['rotate']:.2f} | "
+                     f"{r['gemv']:.2f} |")
     lines.append("")
     lines.append("## Other batch sizes on gate (17408x5120)")
     lines.append("")
@@ -576,8 +589,10 @@ def run_suite(path, argv):
     lines.append("## Decode token stream: 64 layers, base-3, batch 1 (q/k/v and gate/up concatenated)")
     lines.append("")
     t_f, t_s, t_r, t_g = tok["fused"], tok["separate"], tok["rotate_only"], tok["gemv_only"]
-    lines.append(f"- Weight bytes per token: {tok['bytes']:,} ({tok['calls_fused']} product calls).")
-    lines.append(f"- Fused route (tb_linear, rotation in the prologue): {t_f * 1e3:.3f} ms per token = "
+    lines.append(f"- Weight bytes per token: {tok['bytes']:,} ({tok['calls_fused']} product calls, "
+                 f"{tok['launches_fused']} launches).")
+    lines.append(f"- Fused route (tb_linear_ws, rotation in the prologue; down in four parts of K): "
+                 f"{t_f * 1e3:.3f} ms per token = "
                  f"**{1 / t_f:.1f} tokens/s-equivalent**, {tok['bytes'] / t_f / 1e9:.0f} GB/s "
                  f"({100 * tok['bytes'] / t_f / 1e9 / pk:.1f} % of 8 TB/s).")
     lines.append(f"- Separate route (tb_fwht_rotate to fp32, then tb_gemv): {t_s * 1e3:.3f} ms per token = "
@@ -586,8 +601,9 @@ def run_suite(path, argv):
                  f"FWHT share of the separate route = {100 * t_r / (t_r + t_g):.1f} %.")
     lines.append(f"- With true dependencies (each call's input = the previous call's output): "
                  f"{tok['dependent'] * 1e3:.3f} ms per token = {1 / tok['dependent']:.1f} tokens/s with 256 "
-                 f"tb_linear calls; {tok['chained'] * 1e3:.3f} ms = **{1 / tok['chained']:.1f} tokens/s** with "
-                 f"q/k/v -> o -> gate/up in one tb_decode_chain launch per layer (128 launches).")
+                 f"tb_linear_ws calls; {tok['chained'] * 1e3:.3f} ms = **{1 / tok['chained']:.1f} tokens/s** with "
+                 f"q/k/v -> o -> gate/up in one tb_decode_chain launch per layer "
+                 f"({3 * tok['layers']} launches with down's two).")
     lines.append("")
     lines.append("| call | N x K | us per call (fused) | GB/s |")
     lines.append("|---|---|---|---|")
@@ -726,14 +742,15 @@ def main():
             "tokens_per_s_equiv": round(1.0 / t_f, 1), "ms_per_token": round(t_f * 1e3, 4),
             "dependent_tokens_per_s": round(1.0 / token["dependent"], 1),
             "chained_tokens_per_s": round(1.0 / token["chained"], 1),
-            "chained_launches_per_token": 2 * token["layers"],
+            "chained_launches_per_token": 3 * token["layers"],
             "weight_bytes_per_token": token["bytes"], "gbs": round(token["bytes"] / t_f / 1e9, 1),
             "frac_of_hbm_peak": round(token["bytes"] / t_f / 1e9 / HBM_PEAK_GBS, 4),
-            "calls_per_token": token["calls_fused"],
+            "calls_per_token": token["calls_fused"], "launches_per_token": token["launches_fused"],
             "separate_route_ms": round(token["separate"] * 1e3, 4),
             "fwht_share_of_separate_route": round(t_r / (t_r + t_g), 4),
             "workload": "64 layers x (qkv 15360x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408), "
-                        "base-3, batch 1, one HIP graph; tokens_per_s_equiv: tb_linear per call on fixed inputs; "
+                        "base-3, batch 1, one HIP graph; tokens_per_s_equiv: tb_linear_ws per call on fixed inputs "
+                        "(down's rows of K = 17408 in four parts of K, partial sums in the workspace); "
                         "dependent: each call's input is the previous output; chained: the same with "
                         "qkv -> o -> gate_up in one tb_decode_chain launch per layer"}
     print(json.dumps(rec), flush=True)

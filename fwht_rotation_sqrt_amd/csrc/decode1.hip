@@ -270,23 +270,28 @@ __device__ __forceinline__ void transpose_pieces(u32x4 (&r)[4]) {
     }
 }
 
-// The activation part of one linear, for activation wave `wave`: block `wave` of x (one of K/1024),
-// rotated (or copied) into x', then the records of the block's groups 8 wave .. 8 wave + 7 (they
-// read only this block of x').  COHERENT: x is fp32 written by other workgroups of the same
-// launch, read at the device coherence point (no stale cache lines).
+// The activation part of one linear, for activation wave `wave`: block `blk` of x (one of K/1024),
+// rotated (or copied) into x' slot `wave`, then the records of the slot's groups 8 wave ..
+// 8 wave + 7 (they read only this block of x').  blk < 0: a block past the end of the rows (the
+// padding of a K-part), whose x' and records are zero.  COHERENT: x is fp32 written by other
+// workgroups of the same launch, read at the device coherence point (no stale cache lines).
 template <int XDT, bool ROT, bool COHERENT = false>
 __device__ __forceinline__ void prep_linear(const void* __restrict__ x, const uint32_t* __restrict__ sign_bits,
-                                            int wave, int lane, uint32_t xb) {
+                                            int wave, int blk, int lane, uint32_t xb) {
   float xv[16];
+  uint32_t sw = 0;
   if constexpr (COHERENT) {
-    float* xp = const_cast<float*>(static_cast<const float*>(x)) + int64_t(wave) * kBlock + 16 * lane;
+    float* xp = const_cast<float*>(static_cast<const float*>(x)) + int64_t(blk) * kBlock + 16 * lane;
 #pragma unroll
     for (int j = 0; j < 16; ++j) xv[j] = __hip_atomic_load(xp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (ROT) sw = sign_bits[blk * 32 + (lane >> 1)] >> ((lane & 1) * 16);
+  } else if (blk >= 0) {
+    load16<XDT>(x, int64_t(blk) * kBlock + 16 * lane, xv);
+    if constexpr (ROT) sw = sign_bits[blk * 32 + (lane >> 1)] >> ((lane & 1) * 16);
   } else {
-    load16<XDT>(x, int64_t(wave) * kBlock + 16 * lane, xv);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xv[j] = 0.f;
   }
-  uint32_t sw = 0;
-  if constexpr (ROT) sw = sign_bits[wave * 32 + (lane >> 1)] >> ((lane & 1) * 16);
   const uint32_t xblock = xb + uint32_t(kRotScratch * wave);
   if constexpr (ROT) {
 #pragma unroll
@@ -307,16 +312,29 @@ __device__ __forceinline__ void prep_linear(const void* __restrict__ x, const ui
   }
 }
 
+// Where a workgroup's part of K lies in the packed rows: code bytes and scale bytes per row, the
+// part's first code byte and first scale byte within a row, and how many of the part's 4 G4
+// groups exist (fewer only in the last part of a split row: its padding groups have zero
+// activations, and their loads and scales are not read).
+struct RowPart {
+  uint32_t row_bytes, part_off, srow_bytes, spart_off;
+  int real_groups;
+};
+template <int G4>
+__device__ __forceinline__ RowPart whole_rows() {
+  return RowPart{uint32_t(kB3GroupBytes * 4 * G4), 0u, uint32_t(2 * 4 * G4), 0u, 4 * G4};
+}
+
 // The tile part of one linear, for tile wave cw of the workgroup: the decode table (with_table),
 // the weight loads, barrier C (the records are ready), the matrix loop, barrier D, y.  The
 // workgroup takes tiles [t0, t1) (HALVES waves each); lane group kb of the wave of half h walks
-// groups h G4 / HALVES .. of quarter kb of its tile's 16 rows, and the halves' sums meet in LDS.
-template <int G4, int HALVES, int PD = 0, bool COHERENT = false>
+// groups h G4 / HALVES .. of quarter kb of its tile's 16 rows (within the part rp of each row),
+// and the halves' sums meet in LDS.
+template <int G4, int HALVES, int PD = 0, bool COHERENT = false, bool PARTS = false>
 __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-                                            float* __restrict__ y, int n, int t0, int t1, int cw, int lane,
-                                            uint32_t part_lds, bool with_table, int ctid, int cthreads) {
+                                            float* __restrict__ y, int n, const RowPart& rp, int t0, int t1, int cw,
+                                            int lane, uint32_t part_lds, bool with_table, int ctid, int cthreads) {
   constexpr int kGroups = 4 * G4;
-  constexpr int kRowBytes = kB3GroupBytes * kGroups;
   constexpr int kLaneBytes = kB3GroupBytes * G4;             // a quarter of a row
   constexpr int kHG = G4 / HALVES;                            // groups of a quarter per wave
   constexpr int kDw = (13 * kHG + 1) / 2;                     // code dwords a wave's lane reads
@@ -352,27 +370,40 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
   {
     // Each 16-byte load covers 64 contiguous bytes of 16 rows (the four lane groups of a row
     // read consecutive pieces of one quarter); the pieces move to their lane group later.  A
-    // lane without a tile reads past the buffers (zeros): every load is issued on every path.
-    const uint32_t wbytes = uint32_t(n) * kRowBytes, sbytes = uint32_t(n) * (2 * kGroups);
+    // lane without a tile, and a load that starts past the part's last group, reads past the
+    // buffers (zeros): every load is issued on every path.
+    // (whole rows: the row geometry as compile-time constants, and no padding groups)
+    const uint32_t row_bytes = PARTS ? rp.row_bytes : uint32_t(kB3GroupBytes * kGroups);
+    const uint32_t srow_bytes = PARTS ? rp.srow_bytes : uint32_t(2 * kGroups);
+    const uint32_t wbytes = uint32_t(n) * row_bytes, sbytes = uint32_t(n) * srow_bytes;
     const auto wr = rsrc(packed, wbytes);
     const auto sr = rsrc(scales, sbytes);
-    const uint32_t rbase = has_tile ? uint32_t(row) * kRowBytes + uint32_t(4 * d0w) : wbytes;
+    const uint32_t rrow = has_tile ? uint32_t(row) * row_bytes + (PARTS ? rp.part_off : 0u) : wbytes;
+    const uint32_t lim = uint32_t(kB3GroupBytes * rp.real_groups);
+    auto woff = [&](int o) {
+      if constexpr (!PARTS) return rrow + uint32_t(4 * d0w + o);
+      return uint32_t(4 * d0w + o) < lim ? rrow + uint32_t(4 * d0w + o) : wbytes;
+    };
 #pragma unroll
     for (int m = 0; m < kChunks; ++m)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, rbase + uint32_t(kLaneBytes * q + 64 * m + 16 * kb), 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * q + 64 * m + 16 * kb), 0, 0);
         R[m][q] = u32x4{v[0], v[1], v[2], v[3]};
       }
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) {  // the rest of the lane's own dwords
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, rbase + uint32_t(kLaneBytes * kb + 64 * kChunks + 16 * i), 0, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * kb + 64 * kChunks + 16 * i), 0, 0);
       Tl[i] = u32x4{v[0], v[1], v[2], v[3]};
     }
-    // the quarter's G4 scales (the halves take theirs from them)
-    const uint32_t soff = has_tile ? uint32_t(row) * (2 * kGroups) + uint32_t(kb * 2 * G4) : sbytes;
+    // the quarter's G4 scales (the halves take theirs from them); a padding group's scale reads 0
+    const uint32_t srow = has_tile ? uint32_t(row) * srow_bytes + (PARTS ? rp.spart_off : 0u) : sbytes;
 #pragma unroll
-    for (int i = 0; i < (G4 + 1) / 2; ++i) S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff + 4u * i, 0, 0);
+    for (int i = 0; i < (G4 + 1) / 2; ++i) {
+      const uint32_t soff =
+          !PARTS || G4 * kb + 2 * i < rp.real_groups ? srow + uint32_t(2 * G4 * kb + 4 * i) : sbytes;
+      S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
+    }
   }
   lds_barrier();  // C
 
@@ -475,27 +506,46 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
   }
 }
 
-// Kernel.  Waves 0 .. kPrep - 1 prepare the activations (kPrep = K / 1024, one 1024-block each:
+// Kernel.  Waves 0 .. kPrep - 1 prepare the activations (kPrep = 4 G4 / 8, one 1024-block each:
 // rotation, then the records of the block's 8 groups); the tile waves follow, HALVES per tile.
-template <int G4, int HALVES, int XDT, bool ROT>
+// A row of row_groups groups (nblocks 1024-blocks) is split into parts of 4 G4 groups, the last
+// one padded with zero blocks; `grid` workgroups take each part (workgroup w: part w / grid), and
+// part p writes its partial sums to y + p n (one part: y itself).
+template <int G4, int HALVES, int XDT, bool ROT, bool PARTS>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, const void* __restrict__ x,
-    const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int n, int tiles, int nslots, int grid, int nthreads) {
-  constexpr int kPrep = G4 / 2;                               // K / 1024 activation waves
+    const uint32_t* __restrict__ sign_bits, float* __restrict__ y, int n, int tiles, int nslots, int grid, int nthreads,
+    int row_groups, int nblocks) {
+  constexpr int kPrep = G4 / 2;                               // activation waves (1024-blocks of a part)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = PARTS ? int(blockIdx.x) / grid : 0, w = int(blockIdx.x) - part * grid;
   const uint32_t xb = uint32_t(nslots * kSlot);              // x' (fp32, 136 floats per 128-group)
   const uint32_t part_lds = xb + uint32_t(kPrep * kRotScratch);  // halves' partial sums
   if (wave < kPrep) {
-    prep_linear<XDT, ROT>(x, sign_bits, wave, lane, xb);
+    const int blk = kPrep * part + wave;
+    prep_linear<XDT, ROT>(x, sign_bits, wave, !PARTS || blk < nblocks ? blk : -1, lane, xb);
     lds_barrier();  // C: records complete
     lds_barrier();  // D
     return;
   }
-  // workgroup w takes tiles [w T / G, (w + 1) T / G)
-  const int t0 = int((int64_t(blockIdx.x) * tiles) / grid);
-  const int t1 = int((int64_t(blockIdx.x + 1) * tiles) / grid);
-  tile_linear<G4, HALVES>(packed, scales, y, n, t0, t1, wave - kPrep, lane, part_lds, true,
-                          int(threadIdx.x) - 64 * kPrep, nthreads - 64 * kPrep);
+  const int g0 = 4 * G4 * part;
+  const RowPart rp{uint32_t(kB3GroupBytes * row_groups), uint32_t(kB3GroupBytes * g0), uint32_t(2 * row_groups),
+                   uint32_t(2 * g0), min(4 * G4, row_groups - g0)};
+  // workgroup w of the part takes tiles [w T / G, (w + 1) T / G)
+  const int t0 = int((int64_t(w) * tiles) / grid);
+  const int t1 = int((int64_t(w + 1) * tiles) / grid);
+  tile_linear<G4, HALVES, 0, false, PARTS>(packed, scales, y + int64_t(part) * n, n, rp, t0, t1, wave - kPrep, lane,
+                                            part_lds, true, int(threadIdx.x) - 64 * kPrep, nthreads - 64 * kPrep);
+}
+
+// y[i] = sum over parts p in order of part_y[p n + i]: the partial sums of a split row.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part_y, float* __restrict__ y, int n,
+                                                        int parts) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i >= n) return;
+  float acc = part_y[i];
+  for (int p = 1; p < parts; ++p) acc += part_y[int64_t(p) * n + i];
+  y[i] = acc;
 }
 
 // ---------------------------------------------------------------- chained linears
@@ -568,10 +618,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void chain_kernel(ChainArgs a) {
           xprev = a.y[j - 1];
         }
       if (i == 0) {
-        prep_linear<XDT0, true>(a.x0, a.sign_bits, wave, lane, xb);
+        prep_linear<XDT0, true>(a.x0, a.sign_bits, wave, wave, lane, xb);
       } else {
         wait_count(a.sync + i - 1, a.grid, a.spin_limit, status, lane);
-        prep_linear<TB_F32, true, true>(xprev, a.sign_bits, wave, lane, xb);
+        prep_linear<TB_F32, true, true>(xprev, a.sign_bits, wave, wave, lane, xb);
       }
       int t0, t1;
       tile_range(n, t0, t1);
@@ -613,7 +663,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void chain_kernel(ChainArgs a) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int u0 = t0 + r * kTilesPerRound, u1 = min(t1, u0 + kTilesPerRound);
-      tile_linear<G4, 2, 2, true>(packed, scales, y, n, u0, u1, wave - kPrep, ln, part_lds, i == 0 && r == 0,
+      tile_linear<G4, 2, 2, true>(packed, scales, y, n, whole_rows<G4>(), u0, u1, wave - kPrep, ln, part_lds, i == 0 && r == 0,
                                   64 * (wave - kPrep) + ln, a.nthreads - 64 * kPrep);
     }
     __syncthreads();  // this wave's rows of y_i are stored
@@ -633,53 +683,67 @@ int cu_count() {
   return count;
 }
 
-template <int G4, int HALVES, int XDT, bool ROT>
+template <int G4, int HALVES, int XDT, bool ROT, bool PARTS>
 void run_h(const uint8_t* packed, const uint16_t* scales, const void* x, const uint32_t* sign_bits, float* y, int n,
-           int grid, int per_wg, hipStream_t s) {
+           int k, int parts, int grid, int per_wg, hipStream_t s) {
   constexpr int kGroups = 4 * G4;
   const int nw = kGroups / 8 + HALVES * per_wg;  // activation waves (one per 1024-block of x), then tile waves
   const int nslots = max(kTableEntries, kSteps * kGroups + kSteps);
   const size_t lds = size_t(nslots) * kSlot + size_t(kGroups / 8) * kRotScratch + size_t(64) * kMaxWaves;
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode1_kernel<G4, HALVES, XDT, ROT>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode1_kernel<G4, HALVES, XDT, ROT, PARTS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   const int tiles = (n + 15) / 16;
-  decode1_kernel<G4, HALVES, XDT, ROT><<<grid, 64 * nw, lds, s>>>(packed, scales, x, sign_bits, y, n, tiles, nslots, grid,
-                                                                 64 * nw);
+  decode1_kernel<G4, HALVES, XDT, ROT, PARTS><<<parts * grid, 64 * nw, lds, s>>>(
+      packed, scales, x, sign_bits, y, n, tiles, nslots, grid, 64 * nw, k / kGroup, k / kBlock);
 }
 
-// Workgroups and tiles per workgroup for N rows: at most one workgroup per compute unit.
-void plan(int n, int& grid, int& per_wg) {
+// Workgroups per part and tiles per workgroup for N rows in `parts` parts of K: at most one
+// workgroup per compute unit in all.
+void plan(int n, int parts, int& grid, int& per_wg) {
   const int tiles = (n + 15) / 16;
-  grid = min(tiles, cu_count());
+  grid = max(1, min(tiles, cu_count() / parts));
   per_wg = (tiles + grid - 1) / grid;
 }
 
 template <int G4, int XDT, bool ROT>
 void run(const uint8_t* packed, const uint16_t* scales, const void* x, const uint32_t* sign_bits, float* y, int n,
-         hipStream_t s) {
+         int k, int parts, hipStream_t s) {
   int grid, per_wg;
-  plan(n, grid, per_wg);
+  plan(n, parts, grid, per_wg);
   // two waves per tile (each half of K) while they fit in a workgroup, else one
-  if (G4 % 2 == 0 && G4 / 2 >= 1 && (4 * G4) / 8 + 2 * per_wg <= kMaxWaves)
-    run_h<G4, 2, XDT, ROT>(packed, scales, x, sign_bits, y, n, grid, per_wg, s);
-  else
-    run_h<G4, 1, XDT, ROT>(packed, scales, x, sign_bits, y, n, grid, per_wg, s);
+  const bool two = G4 % 2 == 0 && G4 / 2 >= 1 && (4 * G4) / 8 + 2 * per_wg <= kMaxWaves;
+  if (parts == 1) {
+    if (two) run_h<G4, 2, XDT, ROT, false>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
+    else run_h<G4, 1, XDT, ROT, false>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
+  } else if constexpr (G4 >= 6) {  // parts of three to five blocks
+    if (two) run_h<G4, 2, XDT, ROT, true>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
+    else run_h<G4, 1, XDT, ROT, true>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
+  }
 }
 
+// One part of `part_blocks` 1024-blocks (all of K when parts is 1).
 template <int XDT, bool ROT>
-bool dispatch_k(int k, const uint8_t* packed, const uint16_t* scales, const void* x, const uint32_t* sb, float* y,
-                int n, hipStream_t s) {
-  switch (k) {
-    case 1024: run<2, XDT, ROT>(packed, scales, x, sb, y, n, s); return true;
-    case 2048: run<4, XDT, ROT>(packed, scales, x, sb, y, n, s); return true;
-    case 3072: run<6, XDT, ROT>(packed, scales, x, sb, y, n, s); return true;
-    case 4096: run<8, XDT, ROT>(packed, scales, x, sb, y, n, s); return true;
-    case 5120: run<10, XDT, ROT>(packed, scales, x, sb, y, n, s); return true;
+bool dispatch_k(int part_blocks, int k, int parts, const uint8_t* packed, const uint16_t* scales, const void* x,
+                const uint32_t* sb, float* y, int n, hipStream_t s) {
+  switch (part_blocks) {
+    case 1: run<2, XDT, ROT>(packed, scales, x, sb, y, n, k, parts, s); return true;
+    case 2: run<4, XDT, ROT>(packed, scales, x, sb, y, n, k, parts, s); return true;
+    case 3: run<6, XDT, ROT>(packed, scales, x, sb, y, n, k, parts, s); return true;
+    case 4: run<8, XDT, ROT>(packed, scales, x, sb, y, n, k, parts, s); return true;
+    case 5: run<10, XDT, ROT>(packed, scales, x, sb, y, n, k, parts, s); return true;
     default: return false;
   }
+}
+
+// Parts of a row of K (a multiple of 1024): as few as hold at most five blocks each, of equal
+// block counts (the last one padded).
+void split_of(int k, int& parts, int& part_blocks) {
+  const int nb = k / kBlock;
+  parts = decode1_split_parts(1, 1, k);
+  part_blocks = (nb + parts - 1) / parts;
 }
 
 }  // namespace
@@ -688,8 +752,17 @@ bool dispatch_k(int k, const uint8_t* packed, const uint16_t* scales, const void
 bool decode1_supports(int packing, int b, int n, int k) {
   if (packing != 1 || b != 1 || k % kBlock != 0 || k > 5120 || n < 1) return false;
   int grid, per_wg;
-  plan(n, grid, per_wg);
+  plan(n, 1, grid, per_wg);
   return k / kBlock + per_wg <= kMaxWaves;
+}
+
+bool decode1_split_supports(int n, int k) {
+  if (k % kBlock != 0 || k <= 5 * kBlock || n < 1) return false;
+  int parts, part_blocks, grid, per_wg;
+  split_of(k, parts, part_blocks);
+  if (parts > cu_count()) return false;
+  plan(n, parts, grid, per_wg);
+  return part_blocks + per_wg <= kMaxWaves;
 }
 
 namespace {
@@ -755,15 +828,34 @@ bool launch_chain(const tb_chain_linear* lin, int count, const void* x0, int x_d
   return true;
 }
 
+namespace {
+
+bool launch_parts(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt, const uint32_t* sign_bits,
+                  bool rotate, float* y, int n, int k, int parts, int part_blocks, hipStream_t s) {
+  if (rotate) {
+    if (x_dt == TB_F32) return dispatch_k<TB_F32, true>(part_blocks, k, parts, packed, scales, x, sign_bits, y, n, s);
+    if (x_dt == TB_F16) return dispatch_k<TB_F16, true>(part_blocks, k, parts, packed, scales, x, sign_bits, y, n, s);
+    return dispatch_k<TB_BF16, true>(part_blocks, k, parts, packed, scales, x, sign_bits, y, n, s);
+  }
+  if (x_dt == TB_F32) return dispatch_k<TB_F32, false>(part_blocks, k, parts, packed, scales, x, nullptr, y, n, s);
+  return dispatch_k<TB_F16, false>(part_blocks, k, parts, packed, scales, x, nullptr, y, n, s);
+}
+
+}  // namespace
+
 bool launch_decode1(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                     const uint32_t* sign_bits, bool rotate, float* y, int n, int k, hipStream_t s) {
-  if (rotate) {
-    if (x_dt == TB_F32) return dispatch_k<TB_F32, true>(k, packed, scales, x, sign_bits, y, n, s);
-    if (x_dt == TB_F16) return dispatch_k<TB_F16, true>(k, packed, scales, x, sign_bits, y, n, s);
-    return dispatch_k<TB_BF16, true>(k, packed, scales, x, sign_bits, y, n, s);
-  }
-  if (x_dt == TB_F32) return dispatch_k<TB_F32, false>(k, packed, scales, x, nullptr, y, n, s);
-  return dispatch_k<TB_F16, false>(k, packed, scales, x, nullptr, y, n, s);
+  return launch_parts(packed, scales, x, x_dt, sign_bits, rotate, y, n, k, 1, k / kBlock, s);
+}
+
+bool launch_decode1_split(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
+                          const uint32_t* sign_bits, bool rotate, float* y, float* part_y, int n, int k,
+                          hipStream_t s) {
+  int parts, part_blocks;
+  split_of(k, parts, part_blocks);
+  if (!launch_parts(packed, scales, x, x_dt, sign_bits, rotate, part_y, n, k, parts, part_blocks, s)) return false;
+  sum_parts_kernel<<<(n + 255) / 256, 256, 0, s>>>(part_y, y, n, parts);
+  return true;
 }
 
 }  // namespace tb

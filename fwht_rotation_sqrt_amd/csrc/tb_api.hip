@@ -140,7 +140,8 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K) 
   if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(B, 4 * K) ||
       !fits(N, K))
     return -1;
-  return B >= tb::wide_min_batch(packing, N, K) ? 4 * B * K : 0;
+  if (B >= tb::wide_min_batch(packing, N, K)) return 4 * B * K;
+  return 4 * int64_t(tb::decode1_split_parts(packing, B, K)) * N;
 }
 
 int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
@@ -155,8 +156,17 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y) ||
       !aligned16(workspace))
     return TB_ERR_ALIGN;
-  if (x == workspace) return TB_ERR_SHAPE;  // x' is written while x is read by other blocks
+  if (x == workspace) return TB_ERR_SHAPE;  // the workspace is written while x is read by other blocks
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B < tb::wide_min_batch(packing, N, K)) {
+    // batch 1, K past one launch's five blocks: parts of K on separate workgroups, partial sums
+    // in the workspace (rows too many for the parts' workgroups run as tb_linear)
+    if (!tb::decode1_split_supports(int(N), int(K)) ||
+        !tb::launch_decode1_split(packed, scales, x, x_dtype, sign_bits, true, y, static_cast<float*>(workspace),
+                                  int(N), int(K), s))
+      return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+    return finish_launch();
+  }
   tb::launch_fwht(x, x_dtype, workspace, TB_F32, B, K, sign_bits, s);
   tb::launch_gemv_wide(packing, packed, scales, workspace, TB_F32, y, int(B), int(N), int(K), s);
   return finish_launch();
@@ -166,7 +176,12 @@ int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales
                       const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream) {
   const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
   if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
-  if (need > 4 * tb::kStaticScratchFloats) return TB_ERR_SCRATCH;
+  if (need > 4 * tb::kStaticScratchFloats) {
+    // the batch-1 split needs the array only for speed; without room it runs as tb_linear
+    if (B < tb::wide_min_batch(packing, N, K))
+      return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+    return TB_ERR_SCRATCH;
+  }
   void* scratch = nullptr;
   const hipError_t e = tb::static_scratch(&scratch);
   if (e != hipSuccess) {

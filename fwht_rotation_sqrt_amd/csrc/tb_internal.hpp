@@ -54,6 +54,19 @@ void launch_stream_read(const uint8_t* src, int64_t bytes, uint32_t* sink, hipSt
 bool decode1_supports(int packing, int b, int n, int k);
 bool launch_decode1(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
                     const uint32_t* sign_bits, bool rotate, float* y, int n, int k, hipStream_t s);
+// The same product for K > 5120, the rows split into parts of at most five 1024-blocks that
+// separate workgroups take: the number of parts by K alone (0 where no split applies), whether
+// the launch takes the shape (the row tiles of a part fit its workgroups), and the launch, which
+// writes the parts' partial sums to part_y [parts][n] (fp32, device) and then sums them into y in
+// part order (a second launch).
+inline int decode1_split_parts(int packing, int64_t b, int64_t k) {
+  if (packing != 1 || b != 1 || k % kBlock != 0 || k <= 5 * kBlock) return 0;
+  return int((k / kBlock + 4) / 5);
+}
+bool decode1_split_supports(int n, int k);
+bool launch_decode1_split(const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,
+                          const uint32_t* sign_bits, bool rotate, float* y, float* part_y, int n, int k,
+                          hipStream_t s);
 // Chained batch-1 base-3 linears in one launch (decode1.hip): false when the chain is not supported
 // (count, K, or too many tiles per workgroup for a linear).
 bool launch_chain(const tb_chain_linear* lin, int count, const void* x0, int x_dt, const uint32_t* sign_bits, int k,

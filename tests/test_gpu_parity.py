@@ -345,6 +345,46 @@ def test_gemv_linear_batches_above_8(packing):
         tb.tb_linear_ws(packing, pd, sd, xd[:16].contiguous(), sgn, workspace=ws[:need - 16])
 
 
+@pytest.mark.parametrize("n,k,x_dtype", [(300, 6144, "f32"), (777, 11264, "f16"), (5120, 17408, "bf16"),
+                                         (9000, 17408, "bf16"), (12000, 17408, "f32")])
+def test_linear_ws_batch1_rows_in_parts(n, k, x_dtype):
+    """Batch 1, base-3, K above 5120 through tb_linear_ws: the row is taken in parts of K by
+    separate workgroups (6144: two parts of three blocks; 11264: three of four, the last padded
+    by one; 17408, the down projection: four of five, the last padded by three), the partial sums
+    go to the workspace (filled with NaN first: every word must be written) and a second launch
+    adds them.  9000 rows put nine tiles in a workgroup (one wave per tile); 12000 rows are more
+    than the parts' workgroups hold and run as tb_linear.  Sampled rows (every 7th, the first and
+    last 16) against the oracle; tb_linear_noalloc gives the same bits."""
+    note(f"tb_linear_ws batch 1 base3 n={n} k={k} x={x_dtype}")
+    g = synth.rng(275, 0, n % 251, k // 1024)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x32 = g.standard_normal((1, k)).astype(np.float32)
+    if x_dtype == "bf16":
+        xbits = synth.f32_to_bf16_bits(x32)
+        x64, xd = synth.bf16_bits_to_f64(xbits), act_dev(xbits, "bf16")
+    elif x_dtype == "f16":
+        x16 = x32.astype(np.float16)
+        x64, xd = x16.astype(np.float64), dev(x16)
+    else:
+        x64, xd = x32.astype(np.float64), dev(x32)
+    packed, _ = oracle.pack_base3(t)
+    rows = np.unique(np.concatenate([np.arange(0, n, 7), np.arange(16), np.arange(n - 16, n)]))
+    want = oracle.gemv("base3", packed[rows], s[rows], oracle.rotate(x64, signs), k)
+    need = tb.tb_linear_workspace_bytes("base3", 1, n, k)
+    assert need == 4 * n * ((k // 1024 + 4) // 5)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    pd, sd, sgn = dev(packed), scales_dev(s), signs_dev(signs)
+    got = host(tb.tb_linear_ws("base3", pd, sd, xd, sgn, workspace=ws))
+    assert np.isfinite(got).all()
+    assert oracle.rel_err(got[:, rows], want) < TOL
+    y0 = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    assert np.array_equal(host(tb.tb_linear_noalloc("base3", pd, sd, xd, sgn, y0)), got)
+    # the same call again on the same workspace: the same bits (the sums run in part order)
+    assert np.array_equal(host(tb.tb_linear_ws("base3", pd, sd, xd, sgn, workspace=ws)), got)
+
+
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("n", [3 * synth.HIDDEN, 2 * synth.FFN], ids=["qkv_15360", "gate_up_34816"])
 def test_concatenated_linears_sampled_rows(packing, n):
