@@ -51,6 +51,21 @@ def test_noalloc_matches_workspace_entry_point(packing):
         assert oracle.rel_err(a, want) < TOL
 
 
+def test_noalloc_batch1_rows_in_parts():
+    """Batch 1, base-3, K = 17408: the partial sums of the row's four parts of K go to the static
+    array; then a smaller split call (K = 6144, two parts) on the same array.  Same bits as the
+    workspace entry point."""
+    for (n, k), seed in (((700, 17408), 3), ((300, 6144), 4)):
+        note(f"noalloc base3 batch 1 n={n} k={k}")
+        pd, sd, xd, sgn, want = _case("base3", n, k, 1, seed)
+        assert tb.tb_linear_workspace_bytes("base3", 1, n, k) > 0
+        y0 = torch.full((1, n), float("nan"), dtype=torch.float32, device="cuda")
+        _noalloc("base3", pd, sd, xd, sgn, y0)
+        a, b = host(y0), host(tb.tb_linear_ws("base3", pd, sd, xd, sgn))
+        assert np.array_equal(a, b)
+        assert oracle.rel_err(a, want) < TOL
+
+
 def test_noalloc_small_batches_and_limit():
     pd, sd, xd, sgn, want = _case("base3", 64, 2048, 4, 2)
     y = torch.empty((4, 64), dtype=torch.float32, device="cuda")
