@@ -538,13 +538,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode1_kernel(
                                             part_lds, true, int(threadIdx.x) - 64 * kPrep, nthreads - 64 * kPrep);
 }
 
-// y[i] = sum over parts p in order of part_y[p n + i]: the partial sums of a split row.
+// y[i] = sum over parts p in order of part_y[p n + i]: the partial sums of a split row.  Every
+// part's load is issued before the first add (a loop over a runtime count of parts would wait for
+// each load in turn).
+constexpr int kMaxParts = 8;
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part_y, float* __restrict__ y, int n,
                                                         int parts) {
   const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
   if (i >= n) return;
-  float acc = part_y[i];
-  for (int p = 1; p < parts; ++p) acc += part_y[int64_t(p) * n + i];
+  float v[kMaxParts];
+#pragma unroll
+  for (int p = 0; p < kMaxParts; ++p) v[p] = p < parts ? part_y[int64_t(p) * n + i] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int p = 1; p < kMaxParts; ++p)
+    if (p < parts) acc += v[p];
   y[i] = acc;
 }
 
@@ -760,7 +768,7 @@ bool decode1_split_supports(int n, int k) {
   if (k % kBlock != 0 || k <= 5 * kBlock || n < 1) return false;
   int parts, part_blocks, grid, per_wg;
   split_of(k, parts, part_blocks);
-  if (parts > cu_count()) return false;
+  if (parts > kMaxParts || parts > cu_count()) return false;
   plan(n, parts, grid, per_wg);
   return part_blocks + per_wg <= kMaxWaves;
 }
