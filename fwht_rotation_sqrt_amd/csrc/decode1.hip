@@ -37,6 +37,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 namespace tb {
 namespace {
@@ -312,6 +313,12 @@ __device__ __forceinline__ void prep_linear(const void* __restrict__ x, const ui
   }
 }
 
+// f(integral_constant<H>) for the H equal to h, so that H is a compile-time constant inside f.
+template <typename F, int... H>
+__device__ __forceinline__ void dispatch_part(int h, F& f, std::integer_sequence<int, H...>) {
+  ((h == H ? f(std::integral_constant<int, H>{}) : void()), ...);
+}
+
 // Where a workgroup's part of K lies in the packed rows: code bytes and scale bytes per row, the
 // part's first code byte and first scale byte within a row, and how many of the part's 4 G4
 // groups exist (fewer only in the last part of a split row: its padding groups have zero
@@ -489,10 +496,7 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     acc = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
     if (HALVES > 1 && H > 0 && lane < 16) lds_st<float>(part_lds + 4u * uint32_t(16 * (HALVES * tile_in_wg + H) + col), acc);
   };
-  if (has_tile) {
-    if (HALVES == 1 || h == 0) run_half(std::integral_constant<int, 0>{});
-    else run_half(std::integral_constant<int, HALVES - 1>{});
-  }
+  if (has_tile) dispatch_part(h, run_half, std::make_integer_sequence<int, HALVES>{});
   lds_barrier();  // D: the halves' partial sums are in LDS
   if (has_tile && h == 0 && lane < 16) {
 #pragma unroll
@@ -723,7 +727,15 @@ void run(const uint8_t* packed, const uint16_t* scales, const void* x, const uin
   plan(n, parts, grid, per_wg);
   // two waves per tile (each half of K) while they fit in a workgroup, else one
   const bool two = G4 % 2 == 0 && G4 / 2 >= 1 && (4 * G4) / 8 + 2 * per_wg <= kMaxWaves;
+  // five waves per tile (two groups of each quarter each) where K = 5120 leaves room for them:
+  // a workgroup with one or two tiles then runs 14 matrix steps per wave instead of 35 (x' given:
+  // 5120 x 5120 7.05 -> 6.4 us; with the rotation in the prologue the extra waves slow the
+  // prologue as much as they shorten the loop, so that keeps two)
+  const bool five = !ROT && G4 % 5 == 0 && (4 * G4) / 8 + 5 * per_wg <= kMaxWaves;
   if (parts == 1) {
+    if constexpr (G4 % 5 == 0 && !ROT) {
+      if (five) return run_h<G4, 5, XDT, ROT, false>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
+    }
     if (two) run_h<G4, 2, XDT, ROT, false>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
     else run_h<G4, 1, XDT, ROT, false>(packed, scales, x, sign_bits, y, n, k, parts, grid, per_wg, s);
   } else if constexpr (G4 >= 6) {  // parts of three to five blocks
