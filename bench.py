@@ -186,6 +186,28 @@ def bench_decode(d, steps, warmup, smi=True):
     return wall, t_fused, t_gemv, t_rot, sclk
 
 
+def bench_single_1024(steps):
+    """The single 1024x1024 2-bit linear at batch 1 (fp32 x, no outliers): us per call of
+    tb_linear (rotation fused), tb_fwht_rotate and tb_gemv, from graphs of back-to-back calls.  Its
+    0.28 MB of weights stay in cache, so these are latencies, not HBM rates."""
+    n = k = 1024
+    li = synth.linear_inputs(0, n, k, 1, "f32", False)
+    packed = tb.tb_pack_2bit(dev(li.trits))
+    scales = dev(li.scales.view(np.float16))
+    x = dev(li.x)
+    signs = dev(li.signs.view(np.int32))
+    xr = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn in (("tb_linear_us", lambda: tb.tb_linear("2bit", packed, scales, x, signs, y=y)),
+                     ("tb_fwht_rotate_us", lambda: tb.tb_fwht_rotate(x, signs, out=xr)),
+                     ("tb_gemv_us", lambda: tb.tb_gemv("2bit", packed, scales, xr, y=y))):
+        _, g = time_graph(lambda: [fn() for _ in range(steps)], lambda: [fn() for _ in range(3)])
+        out[name] = round(event_time(g) / steps * 1e6, 3)
+        del g
+    return out
+
+
 def bench_gemm(steps, packing="2bit"):
     m, n, k = 512, synth.FFN, synth.HIDDEN
     li = synth.linear_inputs(3, n, k, m, "bf16", True)
@@ -682,6 +704,7 @@ def main():
     gemm = None if args.no_gemm else bench_gemm(args.steps)
     gemm3 = None if args.no_gemm else bench_gemm(args.steps, "base3")
     stream = None if args.no_stream else stream_ceiling(per_copy)
+    single = bench_single_1024(args.steps)
     token = None
     if not args.no_token:
         del d["packed"], d["scales"]
@@ -719,6 +742,7 @@ def main():
                      "frac_of_measured_ceiling": None if stream is None else
                      round(fused_gbs / stream["gbs_at_step_size"], 4)},
         "stream_ceiling": stream,
+        "single_linear_1024x1024_2bit_b1": single,
         "sclk_during_decode": sclk,
         "separate_route_us": {"tb_fwht_rotate_b1_k5120": round(t_rot * 1e6, 3),
                               "tb_fwht_rotate_b1_k17408": round(rotate_k17408_us(), 3),
