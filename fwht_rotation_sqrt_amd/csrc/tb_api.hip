@@ -26,6 +26,12 @@ int finish_launch() {
 
 bool fits(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
 
+// Whether byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + uint64_t(nb) && pb < pa + uint64_t(na);
+}
+
 int check_pack_args(const void* trits, int64_t n, int64_t k, const void* packed) {
   if (n < 0 || k <= 0 || k % tb::kGroup != 0 || !fits(n, k)) return TB_ERR_SHAPE;
   if (n == 0) return TB_OK;
@@ -156,7 +162,9 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y) ||
       !aligned16(workspace))
     return TB_ERR_ALIGN;
-  if (x == workspace) return TB_ERR_SHAPE;  // the workspace is written while x is read by other blocks
+  // the workspace is written while other workgroups still read x, and y is written from it
+  const int64_t xbytes = B * K * (x_dtype == TB_F32 ? 4 : 2);
+  if (overlaps(x, xbytes, workspace, need) || overlaps(y, 4 * B * N, workspace, need)) return TB_ERR_SHAPE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (B < tb::wide_min_batch(packing, N, K)) {
     // batch 1, K past one launch's five blocks: parts of K on separate workgroups, partial sums

@@ -170,8 +170,10 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K);
  * and result as tb_linear, plus workspace: device memory of at least
  * workspace_bytes >= tb_linear_workspace_bytes(packing, B, N, K) bytes (else
  * TB_ERR_WORKSPACE), 16-byte aligned, owned by the caller, overwritten, and
- * not overlapping x.  The library still allocates nothing.  Calls that share
- * a workspace must be ordered (one stream). */
+ * sharing no byte with x or y (else TB_ERR_SHAPE; only the first
+ * tb_linear_workspace_bytes bytes are used and checked).  The library still
+ * allocates nothing.  Calls that share a workspace must be ordered (one
+ * stream). */
 int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
                  const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
                  int64_t workspace_bytes, void* stream);

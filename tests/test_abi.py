@@ -162,6 +162,12 @@ def test_linear_ws_validation():
     assert g(1, P, P, P, 2, None, P, 16, 8, 1024, P, need, None) == NULL
     assert g(1, P, P, P, 2, P, P, 16, 8, 1024, MIS, need, None) == ALIGN
     assert g(1, P, P, P, 2, P, P, 16, 8, 1024, P, need, None) == SHAPE   # x is the workspace
+    Q = P + 0x100000
+    # x [16][1024] bf16 is 32 KiB from P: a workspace starting inside it, or ending inside y
+    assert g(1, P, P, P, 2, P, Q, 16, 8, 1024, P + 0x4000, need, None) == SHAPE
+    assert g(1, P, P, P, 2, P, Q, 16, 8, 1024, Q - need + 16, need, None) == SHAPE
+    # batch 1, base-3, K = 17408: the partial sums (4 x 4 x 8 bytes) may not overlap y either
+    assert g(1, P, P, P, 2, P, Q, 1, 8, 17408, Q + 16, 4 * 4 * 8, None) == SHAPE
     assert g(1, P, P, P, 2, P, P, 16, 0, 1024, P + 0x100000, need, None) == OK   # empty
     # batches the fused kernel serves need no workspace and behave as tb_linear
     assert g(1, P, P, P, 3, P, P, 1, 8, 1024, None, 0, None) == DTYPE
