@@ -85,6 +85,10 @@ int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t r
   if (!x || !xr || !sign_bits) return TB_ERR_NULL;
   if (!aligned16(x) || !aligned16(xr) || !aligned16(sign_bits)) return TB_ERR_ALIGN;
   if (x == xr && x_dtype != xr_dtype) return TB_ERR_DTYPE;
+  // in place works block by block (each block is read whole before it is written); any other
+  // overlap would let one block's output land on another block's input
+  if (x != xr && overlaps(x, rows * K * (x_dtype == TB_F32 ? 4 : 2), xr, rows * K * (xr_dtype == TB_F32 ? 4 : 2)))
+    return TB_ERR_SHAPE;
   tb::launch_fwht(x, x_dtype, xr, xr_dtype, rows, K, sign_bits, static_cast<hipStream_t>(stream));
   return finish_launch();
 }

@@ -111,7 +111,8 @@ int tb_unpack(int packing, const uint8_t* packed, int64_t N, int64_t K, int8_t* 
  * xr_dtype (TB_F32 or TB_F16; fp16 is rounded to nearest even once, at the
  * store).  sign_bits: uint32 [K/32]; bit b of word w is channel 32w+b, set
  * means S = -1; the same mask is used for every row.  Blocks are consecutive
- * 1024-slices of each row.  x == xr is allowed when the dtypes match. */
+ * 1024-slices of each row.  x == xr is allowed when the dtypes match; any
+ * other overlap of x and xr returns TB_ERR_SHAPE. */
 int tb_fwht_rotate(const void* x, int x_dtype, void* xr, int xr_dtype, int64_t rows, int64_t K,
                    const uint32_t* sign_bits, void* stream);
 
