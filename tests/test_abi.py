@@ -73,7 +73,7 @@ def test_rotate_validation():
     assert f(P, 0, P, 2, 2, 1024, P, None) == DTYPE        # bf16 output not offered
     assert f(P, 2, P, 0, 2, 1024, P, None) == DTYPE        # in place needs equal dtypes
     assert f(P, 0, P + 4096, 0, 2, 1024, P, None) == SHAPE  # rows overlap without being in place
-    assert f(P + 4096, 2, P, 1, 2, 1024, P, None) == SHAPE
+    assert f(P + 4096, 2, P + 2048, 1, 2, 1024, P, None) == SHAPE
     assert f(None, 0, P, 0, 2, 1024, P, None) == NULL
     assert f(P, 0, P, 0, 2, 1024, None, None) == NULL
     assert f(P, 0, MIS, 0, 2, 1024, P, None) == ALIGN
