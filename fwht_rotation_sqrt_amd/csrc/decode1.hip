@@ -385,6 +385,16 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     const uint32_t wbytes = uint32_t(n) * row_bytes, sbytes = uint32_t(n) * srow_bytes;
     const auto wr = rsrc(packed, wbytes);
     const auto sr = rsrc(scales, sbytes);
+    // the quarter's G4 scales first (the halves take theirs from them; a padding group's scale
+    // reads 0): loads complete in issue order, so a scale issued after the codes could only be
+    // used once every code load of the wave had arrived
+    const uint32_t srow = has_tile ? uint32_t(row) * srow_bytes + (PARTS ? rp.spart_off : 0u) : sbytes;
+#pragma unroll
+    for (int i = 0; i < (G4 + 1) / 2; ++i) {
+      const uint32_t soff =
+          !PARTS || G4 * kb + 2 * i < rp.real_groups ? srow + uint32_t(2 * G4 * kb + 4 * i) : sbytes;
+      S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
+    }
     const uint32_t rrow = has_tile ? uint32_t(row) * row_bytes + (PARTS ? rp.part_off : 0u) : wbytes;
     const uint32_t lim = uint32_t(kB3GroupBytes * rp.real_groups);
     auto woff = [&](int o) {
@@ -392,24 +402,19 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
       return uint32_t(4 * d0w + o) < lim ? rrow + uint32_t(4 * d0w + o) : wbytes;
     };
 #pragma unroll
-    for (int m = 0; m < kChunks; ++m)
+    for (int m = 0; m < kChunks; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * q + 64 * m + 16 * kb), 0, 0);
         R[m][q] = u32x4{v[0], v[1], v[2], v[3]};
       }
+      // chunk by chunk in issue order, so that waiting for chunk m leaves the later ones in flight
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) {  // the rest of the lane's own dwords
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * kb + 64 * kChunks + 16 * i), 0, 0);
       Tl[i] = u32x4{v[0], v[1], v[2], v[3]};
-    }
-    // the quarter's G4 scales (the halves take theirs from them); a padding group's scale reads 0
-    const uint32_t srow = has_tile ? uint32_t(row) * srow_bytes + (PARTS ? rp.spart_off : 0u) : sbytes;
-#pragma unroll
-    for (int i = 0; i < (G4 + 1) / 2; ++i) {
-      const uint32_t soff =
-          !PARTS || G4 * kb + 2 * i < rp.real_groups ? srow + uint32_t(2 * G4 * kb + 4 * i) : sbytes;
-      S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
     }
   }
   lds_barrier();  // C
@@ -421,18 +426,23 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     constexpr int i0 = H * kHG;                               // first group (of the quarter) of this wave
     constexpr int d0 = (13 * i0 - (i0 & 1)) / 2;              // its first code dword
     uint32_t W[16 * kChunks + 4 * kTailLoads + 1];            // dword d0 + d of the lane's quarter in W[d]
+    // A 64-byte chunk's pieces are moved to their lane groups just before the first step that
+    // needs one of its dwords, so the matrix loop starts on the first chunks while the later ones
+    // are still arriving (waiting for a chunk waits only for the loads issued before it).
+    auto fill = [&](int c) {
+      if (c < kChunks) {
+        transpose_pieces(R[c]);
 #pragma unroll
-    for (int m = 0; m < kChunks; ++m) {
-      transpose_pieces(R[m]);
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+          for (int d = 0; d < 4; ++d) W[16 * c + 4 * p + d] = R[c][p][d];
+      } else {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) W[16 * m + 4 * p + d] = R[m][p][d];
-    }
+        for (int i = 0; i < kTailLoads; ++i)
 #pragma unroll
-    for (int i = 0; i < kTailLoads; ++i)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) W[16 * kChunks + 4 * i + d] = Tl[i][d];
+          for (int d = 0; d < 4; ++d) W[16 * kChunks + 4 * i + d] = Tl[i][d];
+      }
+    };
 
     const uint32_t copy = uint32_t(4 * (lane & 31));
     // A row col of this lane: limb (col & 3) of lane group (col >> 2)'s record; zero records off
@@ -456,10 +466,13 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     auto step_dword = [&](int k) { const int i = group_of(k); return (13 * i - (i & 1)) / 2 + k % kSteps - d0; };
     auto step_reuses_b = [&](int k) { return k > 0 && (group_of(k) & 1) && k % kSteps == 0; };
 
+    // the chunk holding step k's code dword (the tail loads count as the last one)
+    auto chunk_of = [&](int k) { return min(step_dword(k) / 16, kChunks); };
     v8i Bq[kPD + 1];
     u32x4 Alo[kPD + 1], Ahi[kPD + 1];
     auto fetch = [&](int k) {
       const int slot = k % (kPD + 1);
+      if (k == 0 || chunk_of(k) != chunk_of(k - 1)) fill(chunk_of(k));
       if (step_reuses_b(k)) Bq[slot] = Bq[(k - 1) % (kPD + 1)];
       else Bq[slot] = bop(W[step_dword(k)]);
       const uint32_t ab = a_base + uint32_t(group_of(k)) * a_step + uint32_t(kSlot * (k % kSteps));
