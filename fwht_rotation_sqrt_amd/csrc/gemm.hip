@@ -171,12 +171,13 @@ __device__ __forceinline__ void chunk_mma(const ChunkRaw& r, const uint32_t (&s2
 }
 
 // One K-step (one 128-group): chunk kc+1's LDS reads are issued before chunk
-// kc's matrix instructions, so their latency hides behind them.  `ahead`
-// issues the reads of the next K-step's codes and scales, after this step's
-// own reads.
-template <typename Ahead>
+// kc's matrix instructions, so their latency hides behind them.  `mid` (the
+// staging of later steps' operands) runs after the second chunk's matrix
+// instructions are issued, so it overlaps them; `ahead` issues the reads of
+// the next K-step's codes and scales, after this step's own reads.
+template <typename Mid, typename Ahead>
 __device__ __forceinline__ void k_step(const uint32_t (&a_addr)[4], uint32_t buf, const ColBlock (&cb)[5],
-                                       uint32_t tab, floatx4 (&acc)[4][4], floatx4& acc16, Ahead&& ahead) {
+                                       uint32_t tab, floatx4 (&acc)[4][4], floatx4& acc16, Mid&& mid, Ahead&& ahead) {
   uint32_t s2[5];
 #pragma unroll
   for (int c = 0; c < 5; ++c) s2[c] = cb[c].s * 0x10001u;
@@ -189,6 +190,8 @@ __device__ __forceinline__ void k_step(const uint32_t (&a_addr)[4], uint32_t buf
   fetch<2>(a_addr, buf, cb, tab, r0);
   __builtin_amdgcn_sched_barrier(0);
   chunk_mma(r1, s2, acc, acc16);
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
   __builtin_amdgcn_sched_barrier(0);
   fetch<3>(a_addr, buf, cb, tab, r1);
   ahead();
@@ -405,14 +408,20 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   // next scale chunk, then starts the loads for later steps.  The barrier
   // orders LDS traffic only: the loads in flight target registers, so it
   // waits for the LDS counter, not the memory one.
+  // The staging goes in the middle of the step: A buffer p ^ 1 was last read in step g - 1, code
+  // buffer p at the top of step g - 1, and the scale buffer it may write is not the one that
+  // read_b(g + 1) reads, so every wave is done with what it overwrites once barrier g - 1 passed.
   auto step = [&](int g, uint32_t p, const ColBlock (&cb)[5], ColBlock (&nb)[5]) {
-    k_step(a_addr, p * uint32_t(kABuf), cb, tab, acc, acc16, [&] { read_b(g + 1, nb); });
-    store_a(int(p ^ 1u), ra);
-    store_codes(int(p), rc);
-    if (((g + 2) % kSChunk) == 0) store_scales(((g + 2) / kSChunk) & 1, rs);
-    load_a(g + 2, ra);
-    load_codes(g + 3, rc);
-    if (((g + 3) % kSChunk) == 0) load_scales((g + 3) / kSChunk, rs);
+    k_step(a_addr, p * uint32_t(kABuf), cb, tab, acc, acc16,
+           [&] {
+             store_a(int(p ^ 1u), ra);
+             store_codes(int(p), rc);
+             if (((g + 2) % kSChunk) == 0) store_scales(((g + 2) / kSChunk) & 1, rs);
+             load_a(g + 2, ra);
+             load_codes(g + 3, rc);
+             if (((g + 3) % kSChunk) == 0) load_scales((g + 3) / kSChunk, rs);
+           },
+           [&] { read_b(g + 1, nb); });
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
