@@ -230,11 +230,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(scales, uint32_t(n) * uint32_t(groups) * 2u);
   // A staging: load i takes rows 32 i .. 32 i + 31, sixteen threads per
   // 256-byte group row (a wave reads 4 whole rows, 8 full cache lines)
+  // (load i reads 32 i rows past load 0: one register holds the source of all four)
   const int arow = tid >> 4, apiece = tid & 15;
-  uint32_t a_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a_src[i] = m0 + arow + 32 * i < m ? uint32_t((m0 + arow + 32 * i) * k * 2 + apiece * 16) : kNoLoad;
+  const uint32_t a_src = uint32_t((m0 + arow) * k * 2 + apiece * 16);
   const uint32_t a_dst = uint32_t(kAOff + arow * kARowLds + apiece * 16);
   // code staging, 544 16-byte pieces per group; thread tid takes piece tid,
   // and the first 32 threads also piece 512 + tid.
@@ -277,10 +275,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
   // Loads of a group past the end read zeros (offset outside the buffer).
   auto load_a = [&](int g, u32x4 (&ra)[4]) {
     const bool live = g < groups;
+    uint32_t src = a_src;
+    asm volatile("" : "+v"(src));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, a_src[i] == kNoLoad || !live ? kNoLoad : a_src[i] + g * 256,
-                                                    0, 0);
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          xrs, live && m0 + arow + 32 * i < m ? src + uint32_t(64 * i * k + g * 256) : kNoLoad, 0, 0);
   };
   auto store_a = [&](int buf, const u32x4 (&ra)[4]) {
 #pragma unroll
@@ -331,13 +331,19 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_t2_kernel(const uint8_t* __r
     store_piece(c_dst[0] + buf * kCBuf, rc[0], c_hi[0]);
     if (two_pieces) store_piece(c_dst[1] + buf * kCBuf, rc[1], c_hi[1]);
   };
+  // element tid + 512 i sits at row n0 + tid / 8 + 64 i: its source is the first element's plus i
+  // strides of 64 scale rows, so one register serves all five (made opaque at each use: otherwise
+  // the compiler keeps five loop-invariant offsets live across the K loop and spills)
+  const uint32_t s_src = uint32_t(((n0 + (tid >> 3)) * groups + sj) * 2);
   auto load_scales = [&](int chunk, uint32_t (&rs)[5]) {
     const bool live = kSChunk * chunk + sj < groups;
+    uint32_t src = s_src;
+    asm volatile("" : "+v"(src));
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int e = tid + 64 * kWaves * i, row = n0 + (e >> 3);
       rs[i] = __builtin_amdgcn_raw_buffer_load_b16(
-          srs, live && e < kSElems && row < n ? uint32_t((row * groups + kSChunk * chunk + sj) * 2) : kNoLoad, 0, 0);
+          srs, live && e < kSElems && row < n ? src + uint32_t((64 * i * groups + kSChunk * chunk) * 2) : kNoLoad, 0, 0);
     }
   };
   auto store_scales = [&](int buf, const uint32_t (&rs)[5]) {
