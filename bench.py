@@ -581,8 +581,9 @@ def run_suite(path, argv):
     lines.append("")
     lines.append("## Block linears (q/k/v/o 5120x5120, gate/up 17408x5120, down 5120x17408)")
     lines.append("")
-    lines.append("tb_linear_ws differs from tb_linear at batch 8 (one pass over the weights) and for base-3 down "
-                 "at batch 1 (four parts of K on separate workgroups, then a sum of the partial sums).")
+    lines.append("tb_linear_ws differs from tb_linear at batch 8 (x' rotated into the workspace, then tb_gemv's "
+                 "product: one pass over the weights) and for base-3 down at batch 1 (four parts of K on separate "
+                 "workgroups, then a sum of the partial sums).")
     lines.append("")
     lines.append("| linear | N x K | packing | batch | MB | tb_linear us | GB/s | % peak | tb_linear_ws us | GB/s (ws) | "
                  "rotate us | tb_gemv us |")
@@ -597,9 +598,10 @@ def run_suite(path, argv):
     lines.append("## Other batch sizes on gate (17408x5120)")
     lines.append("")
     lines.append("From the measured crossover on (here batch 9 for 2-bit, 8 for base-3), tb_gemv streams the "
-                 "weights once (fp16 matrix cores, gemv_wide.hip); tb_linear_ws rotates into the caller's "
-                 "workspace and does the same; tb_linear (no workspace) runs chunks of 8 rows above 8, each "
-                 "streaming the weights again.")
+                 "weights once (fp16 matrix cores, gemv_wide.hip). tb_linear_ws rotates into the caller's "
+                 "workspace and runs tb_gemv's product from batch 6 (2-bit) or 5 (base-3) on at K = 5120, where "
+                 "that beats the fused kernel's prologue; tb_linear (no workspace) runs the fused kernel up to 8 "
+                 "rows and chunks of 8 rows above, each streaming the weights again.")
     lines.append("")
     lines.append("| packing | batch | tb_linear us | tb_linear_ws us | tb_gemv us | weight GB/s (tb_linear_ws) | "
                  "weight GB/s (tb_gemv) |")

@@ -253,9 +253,10 @@ def tb_linear_workspace_bytes(packing, b: int, n: int, k: int) -> int:
 
 
 def tb_linear_ws(packing, packed, scales, x, sign_bits, workspace=None, y=None, stream=None):
-    """tb_linear with one pass over the weights at every batch; x' (batched calls) or the
-    partial sums of the parts of long base-3 rows (batch 1) go to ``workspace`` (a 16-byte
-    aligned device tensor of at least tb_linear_workspace_bytes bytes)."""
+    """tb_linear with one pass over the weights at every batch; x' (batches from the crossover
+    with the fused kernel on) or the partial sums of the parts of long base-3 rows (batch 1) go
+    to ``workspace`` (a 16-byte aligned device tensor of at least tb_linear_workspace_bytes
+    bytes)."""
     _check(x, "x", tuple(_ACT_DT))
     _rank2(x, "x")
     b, k = x.shape

@@ -40,6 +40,26 @@ int check_pack_args(const void* trits, int64_t n, int64_t k, const void* packed)
   return TB_OK;
 }
 
+// The product y = W x' of tb_gemv on validated arguments: the batched kernel from its crossover
+// on, the batch-1 base-3 kernel where it takes the shape, else the limb kernel in chunks of rows.
+void launch_product(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
+                    int xr_dtype, float* y, int64_t B, int64_t N, int64_t K, hipStream_t s) {
+  if (B >= tb::wide_min_batch(packing, N, K)) {
+    // one pass over the weights on the fp16 matrix cores
+    tb::launch_gemv_wide(packing, packed, scales, xr, xr_dtype, y, int(B), int(N), int(K), s);
+    return;
+  }
+  if (tb::decode1_supports(packing, int(B), int(N), int(K)) &&
+      tb::launch_decode1(packed, scales, xr, xr_dtype, nullptr, false, y, int(N), int(K), s))
+    return;
+  const size_t xsz = xr_dtype == TB_F32 ? 4 : 2;
+  for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
+    const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;
+    tb::launch_gemv(packing, packed, scales, static_cast<const uint8_t*>(xr) + size_t(b0) * size_t(K) * xsz,
+                    xr_dtype, y + b0 * N, int(bc), int(N), int(K), s);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,22 +123,7 @@ int tb_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const vo
   if (N == 0) return TB_OK;
   if (!packed || !scales || !xr || !y) return TB_ERR_NULL;
   if (!aligned16(packed) || !aligned16(scales) || !aligned16(xr) || !aligned16(y)) return TB_ERR_ALIGN;
-  if (B >= tb::wide_min_batch(packing, N, K)) {
-    // one pass over the weights on the fp16 matrix cores
-    tb::launch_gemv_wide(packing, packed, scales, xr, xr_dtype, y, int(B), int(N), int(K),
-                         static_cast<hipStream_t>(stream));
-    return finish_launch();
-  }
-  if (tb::decode1_supports(packing, int(B), int(N), int(K)) &&
-      tb::launch_decode1(packed, scales, xr, xr_dtype, nullptr, false, y, int(N), int(K),
-                         static_cast<hipStream_t>(stream)))
-    return finish_launch();
-  const size_t xsz = xr_dtype == TB_F32 ? 4 : 2;
-  for (int64_t b0 = 0; b0 < B; b0 += TB_GEMV_KERNEL_BATCH) {
-    const int64_t bc = B - b0 < TB_GEMV_KERNEL_BATCH ? B - b0 : TB_GEMV_KERNEL_BATCH;
-    tb::launch_gemv(packing, packed, scales, static_cast<const uint8_t*>(xr) + size_t(b0) * size_t(K) * xsz,
-                    xr_dtype, y + b0 * N, int(bc), int(N), int(K), static_cast<hipStream_t>(stream));
-  }
+  launch_product(packing, packed, scales, xr, xr_dtype, y, B, N, K, static_cast<hipStream_t>(stream));
   return finish_launch();
 }
 
@@ -150,7 +155,7 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K) 
   if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(B, 4 * K) ||
       !fits(N, K))
     return -1;
-  if (B >= tb::wide_min_batch(packing, N, K)) return 4 * B * K;
+  if (B >= tb::separate_min_batch(packing, N, K)) return 4 * B * K;
   return 4 * int64_t(tb::decode1_split_parts(packing, B, K)) * N;
 }
 
@@ -170,7 +175,7 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
   const int64_t xbytes = B * K * (x_dtype == TB_F32 ? 4 : 2);
   if (overlaps(x, xbytes, workspace, need) || overlaps(y, 4 * B * N, workspace, need)) return TB_ERR_SHAPE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (B < tb::wide_min_batch(packing, N, K)) {
+  if (B < tb::separate_min_batch(packing, N, K)) {
     // batch 1, K past one launch's five blocks: parts of K on separate workgroups, partial sums
     // in the workspace (rows too many for the parts' workgroups run as tb_linear)
     if (!tb::decode1_split_supports(int(N), int(K)) ||
@@ -179,8 +184,9 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
       return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
     return finish_launch();
   }
+  // x' in fp32 to the workspace, then tb_gemv's product on it
   tb::launch_fwht(x, x_dtype, workspace, TB_F32, B, K, sign_bits, s);
-  tb::launch_gemv_wide(packing, packed, scales, workspace, TB_F32, y, int(B), int(N), int(K), s);
+  launch_product(packing, packed, scales, workspace, TB_F32, y, B, N, K, s);
   return finish_launch();
 }
 
@@ -189,7 +195,8 @@ int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales
   const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
   if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
   if (need > 4 * tb::kStaticScratchFloats) {
-    // the batch-1 split needs the array only for speed; without room it runs as tb_linear
+    // below the batched product's batch the array serves only speed; without room it runs as
+    // tb_linear
     if (B < tb::wide_min_batch(packing, N, K))
       return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
     return TB_ERR_SCRATCH;

@@ -21,6 +21,15 @@ inline int wide_min_batch(int packing, int64_t n, int64_t k) {
   if (n < 8192) return 7;
   return packing == 0 ? 9 : 8;
 }
+// From this batch on (never past wide_min_batch), tb_linear_ws and tb_linear_noalloc rotate x into
+// the workspace in fp32 and run tb_gemv's product on it (two launches) instead of the one-launch
+// fused kernel, whose activation prologue grows with B K: the measured crossover on the block
+// linears (K = 5120: batch 5 base-3, 6 2-bit; K = 17408: batch 2).
+inline int separate_min_batch(int packing, int64_t n, int64_t k) {
+  const int s = k >= 8192 ? 2 : packing == 0 ? 6 : 5;
+  const int w = wide_min_batch(packing, n, k);
+  return s < w ? s : w;
+}
 constexpr int kWideMaxBatch = 32;    // largest batch of gemv_wide.hip
 constexpr int kWideGemmRows = 96;    // tb_gemm up to this M runs gemv_wide.hip in chunks of 32 rows
 

@@ -151,18 +151,23 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
               const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream);
 
 /* Workspace that tb_linear_ws needs for (packing, B, N, K): 4 B K bytes (x'
- * in fp32) when that call runs on the batched matrix-core product; for base-3
- * weights at batch 1 with K above 5120, 4 P N bytes (the fp32 partial sums of
- * P = ceil(K / 5120) parts of each row, which separate workgroups take); 0 when
- * the one-launch fused kernel of tb_linear serves the call; -1 for an unknown
- * packing, B outside 1..TB_GEMV_MAX_BATCH, N < 0, K not a positive multiple
- * of 1024 or sizes past 32-bit offsets.  Pure host function of its arguments. */
+ * in fp32) when that call rotates into the workspace and runs tb_gemv's product
+ * on it, which is from batch 2 for K >= 8192, else from batch 5 (base-3) or 6
+ * (2-bit), and in any case from the batch at which tb_gemv runs the batched
+ * matrix-core product; for base-3 weights at batch 1 with K above 5120, 4 P N
+ * bytes (the fp32 partial sums of P = ceil(K / 5120) parts of each row, which
+ * separate workgroups take); 0 when the one-launch fused kernel of tb_linear
+ * serves the call; -1 for an unknown packing, B outside 1..TB_GEMV_MAX_BATCH,
+ * N < 0, K not a positive multiple of 1024 or sizes past 32-bit offsets.  Pure
+ * host function of its arguments. */
 int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K);
 
-/* tb_linear with one pass over the weights at every batch: where the batch
- * runs on the batched product (tb_linear_workspace_bytes > 0, B > 1), x' = R_K x
- * is written in fp32 to the caller's workspace and the product reads it, two
- * launches on `stream`.  At batch 1 with base-3 rows longer than 5120 the
+/* tb_linear with one pass over the weights at every batch: where
+ * tb_linear_workspace_bytes > 0 and B > 1, x' = R_K x is written in fp32 to the
+ * caller's workspace and tb_gemv's product reads it, two launches on `stream`
+ * (from those batches on the fused kernel's activation prologue costs more than
+ * the separate rotation; above 8 rows the product is the batched one, which
+ * streams the weights once).  At batch 1 with base-3 rows longer than 5120 the
  * fused one-launch kernel takes the rows in parts of K on separate workgroups
  * (all compute units busy where the rows alone are too few), writes each
  * part's partial sums to the workspace and a second launch adds them in part
@@ -185,8 +190,9 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
  * tb_linear_workspace_bytes(packing, B, N, K) > 0, x' goes to a static device
  * array of the library (4 MiB per GPU, held until the process ends) instead of
  * a caller workspace; the call returns TB_ERR_SCRATCH when it would need more
- * (B K > 2^20 floats), except that a batch-1 call whose partial sums do not fit
- * runs as tb_linear.  Otherwise it is exactly tb_linear.  Same arguments,
+ * (B K > 2^20 floats), except that a call below the batch of tb_gemv's batched
+ * product (partial sums of batch 1, or x' of a few rows) runs as tb_linear
+ * when the array cannot hold it.  Otherwise it is exactly tb_linear.  Same arguments,
  * kernels and result as tb_linear_ws.  Every call on one GPU shares that
  * array: calls that overlap on one GPU (different streams without ordering,
  * or several host threads) race on it; order them on one stream.  x' and the

@@ -134,16 +134,21 @@ def test_gemm_validation():
 def test_linear_workspace_bytes():
     lib = tb.library()
     f = lib.tb_linear_workspace_bytes
-    # (packing, B, N, K): the fused one-launch kernel below the measured crossover, x' in fp32 above
+    # (packing, B, N, K): the fused one-launch kernel below the measured crossover, x' in fp32 from
+    # it on (K >= 8192: batch 2; else batch 5 base-3, 6 2-bit; never past the batched product's)
     assert f(0, 1, 17408, 5120) == 0 and f(1, 1, 17408, 5120) == 0
-    assert f(0, 8, 17408, 5120) == 0 and f(0, 9, 17408, 5120) == 4 * 9 * 5120
-    assert f(1, 7, 17408, 5120) == 0 and f(1, 8, 17408, 5120) == 4 * 8 * 5120
-    assert f(0, 6, 5120, 5120) == 0 and f(0, 7, 5120, 5120) == 4 * 7 * 5120
-    assert f(1, 4, 5120, 17408) == 0 and f(1, 5, 5120, 17408) == 4 * 5 * 17408
+    assert f(0, 5, 17408, 5120) == 0 and f(0, 6, 17408, 5120) == 4 * 6 * 5120
+    assert f(0, 9, 17408, 5120) == 4 * 9 * 5120
+    assert f(1, 4, 17408, 5120) == 0 and f(1, 5, 17408, 5120) == 4 * 5 * 5120
+    assert f(0, 5, 5120, 5120) == 0 and f(0, 6, 5120, 5120) == 4 * 6 * 5120
+    assert f(1, 4, 5120, 5120) == 0 and f(1, 5, 5120, 5120) == 4 * 5 * 5120
+    assert f(0, 1, 5120, 17408) == 0 and f(0, 2, 5120, 17408) == 4 * 2 * 17408
+    assert f(1, 2, 5120, 17408) == 4 * 2 * 17408 and f(1, 2, 300, 8192) == 4 * 2 * 8192
+    assert f(1, 4, 300, 7168) == 0 and f(1, 5, 300, 7168) == 4 * 5 * 7168
     # base-3 batch 1 with K past five 1024-blocks: partial sums of ceil(K / 5120) parts of K
     assert f(1, 1, 5120, 17408) == 4 * 4 * 5120 and f(1, 1, 5120, 6144) == 4 * 2 * 5120
     assert f(1, 1, 777, 11264) == 4 * 3 * 777 and f(1, 1, 40000, 17408) == 4 * 4 * 40000
-    assert f(0, 1, 5120, 17408) == 0 and f(1, 2, 5120, 17408) == 0 and f(1, 1, 5120, 5120) == 0
+    assert f(1, 1, 5120, 5120) == 0
     assert f(1, 32, 5120, 17408) == 4 * 32 * 17408
     assert f(1, 33, 8, 1024) == -1 and f(1, 0, 8, 1024) == -1 and f(1, 4, 8, 1152) == -1
     assert f(2, 4, 8, 1024) == -1 and f(1, 4, -1, 1024) == -1

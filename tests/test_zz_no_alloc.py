@@ -38,8 +38,9 @@ def _noalloc(packing, pd, sd, xd, sgn, y):
 
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 def test_noalloc_matches_workspace_entry_point(packing):
-    # call 1: 32 rows of K = 17408 (2.2 MB of the 4 MiB scratch); call 2: 9 rows of K = 3072
-    for (n, k, rows), seed in (((300, 17408, 32), 0), ((200, 3072, 9), 1)):
+    # call 1: 32 rows of K = 17408 (2.2 MB of the 4 MiB scratch); call 2: 9 rows of K = 3072;
+    # call 3: 6 rows of K = 5120 (x' rotated into the array, then the limb product)
+    for (n, k, rows), seed in (((300, 17408, 32), 0), ((200, 3072, 9), 1), ((500, 5120, 6), 2)):
         note(f"noalloc {packing} n={n} k={k} rows={rows}")
         pd, sd, xd, sgn, want = _case(packing, n, k, rows, seed)
         assert tb.tb_linear_workspace_bytes(packing, rows, n, k) > 0   # the call uses the scratch
