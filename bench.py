@@ -582,7 +582,8 @@ def run_suite(path, argv):
     lines.append("## Block linears (q/k/v/o 5120x5120, gate/up 17408x5120, down 5120x17408)")
     lines.append("")
     lines.append("tb_linear_ws differs from tb_linear at batch 8 (x' rotated into the workspace, then tb_gemv's "
-                 "product: one pass over the weights) and for base-3 down at batch 1 (four parts of K on separate "
+                 "product: one pass over the weights; at 5120 rows the batched product takes K in four parts and "
+                 "adds their partial sums) and for base-3 down at batch 1 (four parts of K on separate "
                  "workgroups, then a sum of the partial sums).")
     lines.append("")
     lines.append("| linear | N x K | packing | batch | MB | tb_linear us | GB/s | % peak | tb_linear_ws us | GB/s (ws) | "

@@ -887,8 +887,12 @@ bool launch_decode1_split(const uint8_t* packed, const uint16_t* scales, const v
   int parts, part_blocks;
   split_of(k, parts, part_blocks);
   if (!launch_parts(packed, scales, x, x_dt, sign_bits, rotate, part_y, n, k, parts, part_blocks, s)) return false;
-  sum_parts_kernel<<<(n + 255) / 256, 256, 0, s>>>(part_y, y, n, parts);
+  launch_sum_parts(part_y, y, n, parts, s);
   return true;
+}
+
+void launch_sum_parts(const float* part_y, float* y, int count, int parts, hipStream_t s) {
+  sum_parts_kernel<<<(count + 255) / 256, 256, 0, s>>>(part_y, y, count, parts);
 }
 
 }  // namespace tb

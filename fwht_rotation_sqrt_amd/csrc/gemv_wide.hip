@@ -197,7 +197,7 @@ template <int PACK, int XF32, int MB, int T, int NW>
 __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const void* __restrict__ xr, float* __restrict__ y,
-                                                            int nb, int n, int k) {
+                                                            int nb, int n, int k, int rb, int gpp) {
   constexpr int kGroupBytes = PACK == 0 ? 32 : kB3GroupBytes;
   constexpr int kXsz = XF32 ? 4 : 2;
   constexpr uint32_t kTab = 0;  // the reduction area reuses the table's LDS once every wave has left the loop
@@ -208,9 +208,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   const __amdgpu_buffer_rsrc_t srs = rsrc(scales, uint32_t(n) * uint32_t(groups) * 2u);
   const __amdgpu_buffer_rsrc_t xrs = rsrc(xr, uint32_t(nb) * uint32_t(k) * kXsz);
 
-  // this wave's groups
-  const int per_wave = (groups + NW - 1) / NW;
-  const int g0 = min(groups, wave * per_wave), g1 = min(groups, g0 + per_wave);
+  // This workgroup's part of K: groups [gp0, gp1) (part blockIdx / rb; one part: all of K), with its
+  // partial sums at y + part B N; then this wave's groups of the part.
+  const int part = int(blockIdx.x) / rb, blk = int(blockIdx.x) - part * rb;
+  const int gp0 = min(groups, part * gpp), gp1 = min(groups, gp0 + gpp);
+  y += size_t(part) * size_t(nb) * size_t(n);
+  const int per_wave = (gp1 - gp0 + NW - 1) / NW;
+  const int g0 = min(gp1, gp0 + wave * per_wave), g1 = min(gp1, g0 + per_wave);
 
   // Per-lane offsets of group 0.  Rows past n and activation rows past nb
   // fall outside their buffers and read zero, and so does every group at or
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
   // wave-uniform strides further; with up to 3 tiles the T offsets are kept
   // in registers, with more they are recomputed at each load (registers).
   constexpr bool kEarly = T <= 3;  // also: all next-group weight loads at the group start
-  const int tile0 = blockIdx.x * T;
+  const int tile0 = blk * T;
   const uint32_t row0 = uint32_t(16 * tile0 + r);
   const uint32_t wbase = row0 * row_bytes + uint32_t(PACK == 0 ? 8 * q : 6 * q), wstride = 16u * row_bytes;
   const uint32_t sbase = row0 * uint32_t(groups) * 2u, sstride = 32u * uint32_t(groups);
@@ -380,7 +384,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_wide_kernel(const uint8_t* __res
 }
 
 template <int PACK, int XF32, int MB, int T>
-void run(const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k, hipStream_t s) {
+void run(const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k, int parts,
+         hipStream_t s) {
   constexpr int NW = kWaves;
   constexpr int kRed = NW * T * MB * kRedSlot;
   constexpr int lds = PACK == 1 && kTableBytes > kRed ? kTableBytes : kRed;
@@ -390,47 +395,55 @@ void run(const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, i
     return true;
   }();
   (void)attr;
-  const int tiles = (n + 15) / 16;
-  gemv_wide_kernel<PACK, XF32, MB, T, NW><<<(tiles + T - 1) / T, 64 * NW, lds, s>>>(p, sc, x, y, b, n, k);
+  const int tiles = (n + 15) / 16, rb = (tiles + T - 1) / T, groups = k / kGroup;
+  gemv_wide_kernel<PACK, XF32, MB, T, NW><<<rb * parts, 64 * NW, lds, s>>>(p, sc, x, y, b, n, k, rb,
+                                                                          (groups + parts - 1) / parts);
 }
 
 template <int PACK, int XF32, int MB>
-void run_t(int t, const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k,
+void run_t(int t, const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k, int parts,
            hipStream_t s) {
   switch (t) {
-    case 1: run<PACK, XF32, MB, 1>(p, sc, x, y, b, n, k, s); break;
-    case 2: run<PACK, XF32, MB, 2>(p, sc, x, y, b, n, k, s); break;
-    case 3: run<PACK, XF32, MB, 3>(p, sc, x, y, b, n, k, s); break;
-    case 4: run<PACK, XF32, MB, 4>(p, sc, x, y, b, n, k, s); break;
-    default: run<PACK, XF32, MB, 5>(p, sc, x, y, b, n, k, s); break;
+    case 1: run<PACK, XF32, MB, 1>(p, sc, x, y, b, n, k, parts, s); break;
+    case 2: run<PACK, XF32, MB, 2>(p, sc, x, y, b, n, k, parts, s); break;
+    case 3: run<PACK, XF32, MB, 3>(p, sc, x, y, b, n, k, parts, s); break;
+    case 4: run<PACK, XF32, MB, 4>(p, sc, x, y, b, n, k, parts, s); break;
+    default: run<PACK, XF32, MB, 5>(p, sc, x, y, b, n, k, parts, s); break;
   }
 }
 
 template <int PACK>
 void run_pack(int xr_dt, const uint8_t* p, const uint16_t* sc, const void* x, float* y, int b, int n, int k,
-              hipStream_t s) {
+              int parts, hipStream_t s) {
   // tiles per workgroup: the fewest that keep the grid within one workgroup per compute unit
   // (at most 5); two workgroups per unit with fewer tiles each ran 20-80 % slower at every shape
   // and batch (each workgroup fetches the whole activation block, and the operands built from it
-  // serve fewer tiles)
+  // serve fewer tiles).  In parts of K, five tiles per workgroup (wide_parts fills the units).
   const int tiles = (n + 15) / 16;
-  const int t = std::min(5, std::max(1, (tiles + 255) / 256));
+  const int t = parts > 1 ? 5 : std::min(5, std::max(1, (tiles + 255) / 256));
   const bool f32 = xr_dt == 0;
   if (b <= 16) {
-    if (f32) run_t<PACK, 1, 1>(t, p, sc, x, y, b, n, k, s);
-    else run_t<PACK, 0, 1>(t, p, sc, x, y, b, n, k, s);
+    if (f32) run_t<PACK, 1, 1>(t, p, sc, x, y, b, n, k, parts, s);
+    else run_t<PACK, 0, 1>(t, p, sc, x, y, b, n, k, parts, s);
   } else {
-    if (f32) run_t<PACK, 1, 2>(t, p, sc, x, y, b, n, k, s);
-    else run_t<PACK, 0, 2>(t, p, sc, x, y, b, n, k, s);
+    if (f32) run_t<PACK, 1, 2>(t, p, sc, x, y, b, n, k, parts, s);
+    else run_t<PACK, 0, 2>(t, p, sc, x, y, b, n, k, parts, s);
   }
 }
 
 }  // namespace
 
 void launch_gemv_wide(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr, int xr_dt,
-                      float* y, int b, int n, int k, hipStream_t s) {
-  if (packing == 0) run_pack<0>(xr_dt, packed, scales, xr, y, b, n, k, s);
-  else run_pack<1>(xr_dt, packed, scales, xr, y, b, n, k, s);
+                      float* y, int b, int n, int k, hipStream_t s, float* part_y, int parts) {
+  if (parts > 1 && part_y) {
+    // parts of K on separate workgroups, partial sums to part_y [parts][b][n], then added in order
+    if (packing == 0) run_pack<0>(xr_dt, packed, scales, xr, part_y, b, n, k, parts, s);
+    else run_pack<1>(xr_dt, packed, scales, xr, part_y, b, n, k, parts, s);
+    launch_sum_parts(part_y, y, b * n, parts, s);
+    return;
+  }
+  if (packing == 0) run_pack<0>(xr_dt, packed, scales, xr, y, b, n, k, 1, s);
+  else run_pack<1>(xr_dt, packed, scales, xr, y, b, n, k, 1, s);
 }
 
 }  // namespace tb

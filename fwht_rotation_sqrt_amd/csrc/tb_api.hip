@@ -60,6 +60,45 @@ void launch_product(int packing, const uint8_t* packed, const uint16_t* scales, 
   }
 }
 
+// tb_linear_ws; without allow_parts the batched product takes whole rows (workspace: x' only).
+int linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
+              const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
+              int64_t workspace_bytes, bool allow_parts, void* stream) {
+  int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
+  const int parts = allow_parts && need > 0 && B >= tb::wide_min_batch(packing, N, K) ? tb::wide_parts(B, N, K) : 1;
+  if (!allow_parts && need > 0 && B >= tb::wide_min_batch(packing, N, K)) need = 4 * B * K;
+  if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+  if (x_dtype != TB_F32 && x_dtype != TB_F16 && x_dtype != TB_BF16) return TB_ERR_DTYPE;
+  if (workspace_bytes < need) return TB_ERR_WORKSPACE;
+  if (N == 0) return TB_OK;
+  if (!packed || !scales || !x || !sign_bits || !y || !workspace) return TB_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y) ||
+      !aligned16(workspace))
+    return TB_ERR_ALIGN;
+  // the workspace is written while other workgroups still read x, and y is written from it
+  const int64_t xbytes = B * K * (x_dtype == TB_F32 ? 4 : 2);
+  if (overlaps(x, xbytes, workspace, need) || overlaps(y, 4 * B * N, workspace, need)) return TB_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B < tb::separate_min_batch(packing, N, K)) {
+    // batch 1, K past one launch's five blocks: parts of K on separate workgroups, partial sums
+    // in the workspace (rows too many for the parts' workgroups run as tb_linear)
+    if (!tb::decode1_split_supports(int(N), int(K)) ||
+        !tb::launch_decode1_split(packed, scales, x, x_dtype, sign_bits, true, y, static_cast<float*>(workspace),
+                                  int(N), int(K), s))
+      return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+    return finish_launch();
+  }
+  // x' in fp32 to the workspace, then tb_gemv's product on it (the batched one in parts of K, with
+  // the partial sums after x')
+  tb::launch_fwht(x, x_dtype, workspace, TB_F32, B, K, sign_bits, s);
+  if (parts > 1)
+    tb::launch_gemv_wide(packing, packed, scales, workspace, TB_F32, y, int(B), int(N), int(K), s,
+                         reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 4 * B * K), parts);
+  else
+    launch_product(packing, packed, scales, workspace, TB_F32, y, B, N, K, s);
+  return finish_launch();
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +194,11 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K) 
   if (B < 1 || B > TB_GEMV_MAX_BATCH || N < 0 || K <= 0 || K % tb::kBlock != 0 || !fits(B, 4 * K) ||
       !fits(N, K))
     return -1;
+  if (B >= tb::wide_min_batch(packing, N, K)) {
+    // x' in fp32, then the partial sums of the batched product's parts of K
+    const int parts = tb::wide_parts(B, N, K);
+    return 4 * B * K + (parts > 1 ? 4 * int64_t(parts) * B * N : 0);
+  }
   if (B >= tb::separate_min_batch(packing, N, K)) return 4 * B * K;
   return 4 * int64_t(tb::decode1_split_parts(packing, B, K)) * N;
 }
@@ -162,44 +206,24 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K) 
 int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
                  const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
                  int64_t workspace_bytes, void* stream) {
-  const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
-  if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
-  if (x_dtype != TB_F32 && x_dtype != TB_F16 && x_dtype != TB_BF16) return TB_ERR_DTYPE;
-  if (workspace_bytes < need) return TB_ERR_WORKSPACE;
-  if (N == 0) return TB_OK;
-  if (!packed || !scales || !x || !sign_bits || !y || !workspace) return TB_ERR_NULL;
-  if (!aligned16(packed) || !aligned16(scales) || !aligned16(x) || !aligned16(sign_bits) || !aligned16(y) ||
-      !aligned16(workspace))
-    return TB_ERR_ALIGN;
-  // the workspace is written while other workgroups still read x, and y is written from it
-  const int64_t xbytes = B * K * (x_dtype == TB_F32 ? 4 : 2);
-  if (overlaps(x, xbytes, workspace, need) || overlaps(y, 4 * B * N, workspace, need)) return TB_ERR_SHAPE;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (B < tb::separate_min_batch(packing, N, K)) {
-    // batch 1, K past one launch's five blocks: parts of K on separate workgroups, partial sums
-    // in the workspace (rows too many for the parts' workgroups run as tb_linear)
-    if (!tb::decode1_split_supports(int(N), int(K)) ||
-        !tb::launch_decode1_split(packed, scales, x, x_dtype, sign_bits, true, y, static_cast<float*>(workspace),
-                                  int(N), int(K), s))
-      return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
-    return finish_launch();
-  }
-  // x' in fp32 to the workspace, then tb_gemv's product on it
-  tb::launch_fwht(x, x_dtype, workspace, TB_F32, B, K, sign_bits, s);
-  launch_product(packing, packed, scales, workspace, TB_F32, y, B, N, K, s);
-  return finish_launch();
+  return linear_ws(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, workspace, workspace_bytes, true,
+                   stream);
 }
 
 int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dtype,
                       const uint32_t* sign_bits, float* y, int64_t B, int64_t N, int64_t K, void* stream) {
-  const int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
+  int64_t need = tb_linear_workspace_bytes(packing, B, N, K);
   if (need <= 0) return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
+  bool allow_parts = true;
   if (need > 4 * tb::kStaticScratchFloats) {
     // below the batched product's batch the array serves only speed; without room it runs as
-    // tb_linear
+    // tb_linear.  The batched product's partial sums, too; without room for them it takes whole
+    // rows, which need x' only.
     if (B < tb::wide_min_batch(packing, N, K))
       return tb_linear(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, stream);
-    return TB_ERR_SCRATCH;
+    if (4 * B * K > 4 * tb::kStaticScratchFloats) return TB_ERR_SCRATCH;
+    allow_parts = false;
+    need = 4 * B * K;
   }
   void* scratch = nullptr;
   const hipError_t e = tb::static_scratch(&scratch);
@@ -208,7 +232,7 @@ int tb_linear_noalloc(int packing, const uint8_t* packed, const uint16_t* scales
              hipGetErrorString(e));
     return TB_ERR_HIP;
   }
-  return tb_linear_ws(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, scratch, need, stream);
+  return linear_ws(packing, packed, scales, x, x_dtype, sign_bits, y, B, N, K, scratch, need, allow_parts, stream);
 }
 
 int tb_decode_chain(int packing, const tb_chain_linear* linears, int count, const void* x0, int x_dtype,

@@ -43,8 +43,28 @@ void launch_fwht(const void* x, int x_dt, void* y, int y_dt, int64_t rows, int64
                  const uint32_t* sign_bits, hipStream_t s);
 void launch_gemv(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr,
                  int xr_dt, float* y, int b, int n, int k, hipStream_t s);
+// The batched product; with part_y (fp32 [parts][b][n], device) and parts > 1 it takes K in parts on
+// separate workgroups and then adds the parts' partial sums into y in part order (second launch).
 void launch_gemv_wide(int packing, const uint8_t* packed, const uint16_t* scales, const void* xr, int xr_dt,
-                      float* y, int b, int n, int k, hipStream_t s);
+                      float* y, int b, int n, int k, hipStream_t s, float* part_y = nullptr, int parts = 1);
+// Parts of K for the batched product where the caller has room for partial sums (tb_linear_ws):
+// each workgroup reads the activations of its whole K range, so rows too few to fill the 256
+// compute units with five-tile workgroups are taken in parts of K instead of in smaller
+// workgroups (each part's workgroups read only that part of the activations).  At most 8 parts
+// and at least 8 groups per part; 1 where whole rows fill the units, and two parts only from
+// batch 16 (below it the second launch that adds the parts cost more than two parts saved).
+// Pure function of the shape.
+inline int wide_parts(int64_t b, int64_t n, int64_t k) {
+  constexpr int64_t kUnits = 256, kTilesPerWg = 5;
+  const int64_t rb = ((n + 15) / 16 + kTilesPerWg - 1) / kTilesPerWg;
+  int64_t p = rb > 0 ? kUnits / rb : 1;
+  p = p < (k / kGroup) / 8 ? p : (k / kGroup) / 8;
+  p = p < 8 ? p : 8;
+  if (p == 2 && b < 16) p = 1;
+  return p >= 2 ? int(p) : 1;
+}
+// y[i] = sum over parts p in order of part_y[p count + i] (fp32, device), i < count.
+void launch_sum_parts(const float* part_y, float* y, int count, int parts, hipStream_t s);
 void launch_gemm(int packing, const uint8_t* packed, const uint16_t* scales, const uint16_t* xr, float* y,
                  int m, int n, int k, hipStream_t s);
 void launch_linear(int packing, const uint8_t* packed, const uint16_t* scales, const void* x, int x_dt,

@@ -154,7 +154,11 @@ int tb_linear(int packing, const uint8_t* packed, const uint16_t* scales, const 
  * in fp32) when that call rotates into the workspace and runs tb_gemv's product
  * on it, which is from batch 2 for K >= 8192, else from batch 5 (base-3) or 6
  * (2-bit), and in any case from the batch at which tb_gemv runs the batched
- * matrix-core product; for base-3 weights at batch 1 with K above 5120, 4 P N
+ * matrix-core product; from that batch on, plus 4 P B N bytes where the rows
+ * are too few to fill the compute units with five row tiles per workgroup and
+ * the product takes K in P parts on separate workgroups (P = 2..8: the fp32
+ * partial sums of each part, e.g. 4 parts for 5120 rows; P = 2 only from batch
+ * 16); for base-3 weights at batch 1 with K above 5120, 4 P N
  * bytes (the fp32 partial sums of P = ceil(K / 5120) parts of each row, which
  * separate workgroups take); 0 when the one-launch fused kernel of tb_linear
  * serves the call; -1 for an unknown packing, B outside 1..TB_GEMV_MAX_BATCH,
@@ -167,7 +171,9 @@ int64_t tb_linear_workspace_bytes(int packing, int64_t B, int64_t N, int64_t K);
  * caller's workspace and tb_gemv's product reads it, two launches on `stream`
  * (from those batches on the fused kernel's activation prologue costs more than
  * the separate rotation; above 8 rows the product is the batched one, which
- * streams the weights once).  At batch 1 with base-3 rows longer than 5120 the
+ * streams the weights once, and with few rows takes K in parts whose partial
+ * sums a third launch adds in part order, so the result does not depend on
+ * timing).  At batch 1 with base-3 rows longer than 5120 the
  * fused one-launch kernel takes the rows in parts of K on separate workgroups
  * (all compute units busy where the rows alone are too few), writes each
  * part's partial sums to the workspace and a second launch adds them in part
@@ -189,10 +195,12 @@ int tb_linear_ws(int packing, const uint8_t* packed, const uint16_t* scales, con
  * tight serving loops, harnesses that forbid hipMalloc).  Where
  * tb_linear_workspace_bytes(packing, B, N, K) > 0, x' goes to a static device
  * array of the library (4 MiB per GPU, held until the process ends) instead of
- * a caller workspace; the call returns TB_ERR_SCRATCH when it would need more
- * (B K > 2^20 floats), except that a call below the batch of tb_gemv's batched
- * product (partial sums of batch 1, or x' of a few rows) runs as tb_linear
- * when the array cannot hold it.  Otherwise it is exactly tb_linear.  Same arguments,
+ * a caller workspace.  The call returns TB_ERR_SCRATCH when x' alone would need
+ * more (B K > 2^20 floats), except that a call below the batch of tb_gemv's
+ * batched product (partial sums of batch 1, or x' of a few rows) runs as
+ * tb_linear when the array cannot hold it, and a batched call whose x' fits
+ * but whose parts' partial sums do not takes whole rows (the same result up to
+ * rounding: another summation order).  Otherwise it has the same arguments,
  * kernels and result as tb_linear_ws.  Every call on one GPU shares that
  * array: calls that overlap on one GPU (different streams without ordering,
  * or several host threads) race on it; order them on one stream.  x' and the

@@ -149,7 +149,16 @@ def test_linear_workspace_bytes():
     assert f(1, 1, 5120, 17408) == 4 * 4 * 5120 and f(1, 1, 5120, 6144) == 4 * 2 * 5120
     assert f(1, 1, 777, 11264) == 4 * 3 * 777 and f(1, 1, 40000, 17408) == 4 * 4 * 40000
     assert f(1, 1, 5120, 5120) == 0
-    assert f(1, 32, 5120, 17408) == 4 * 32 * 17408
+    # from the batched product's batch on, x' plus the partial sums of its parts of K where the rows
+    # are too few for five-tile workgroups on every compute unit (5120 rows: four parts; 9000 rows:
+    # two parts from batch 16; 17408 rows: whole rows)
+    assert f(1, 32, 5120, 17408) == 4 * 32 * 17408 + 4 * 4 * 32 * 5120
+    assert f(1, 8, 5120, 5120) == 4 * 8 * 5120 + 4 * 4 * 8 * 5120
+    assert f(1, 8, 300, 17408) == 4 * 8 * 17408 + 4 * 8 * 8 * 300       # 8 parts (at most 8)
+    assert f(1, 8, 300, 2048) == 4 * 8 * 2048                           # 16 groups: 2 parts below 16 rows
+    assert f(1, 16, 300, 2048) == 4 * 16 * 2048 + 4 * 2 * 16 * 300
+    assert f(0, 9, 9000, 5120) == 4 * 9 * 5120 and f(0, 16, 9000, 5120) == 4 * 16 * 5120 + 4 * 2 * 16 * 9000
+    assert f(1, 32, 17408, 5120) == 4 * 32 * 5120
     assert f(1, 33, 8, 1024) == -1 and f(1, 0, 8, 1024) == -1 and f(1, 4, 8, 1152) == -1
     assert f(2, 4, 8, 1024) == -1 and f(1, 4, -1, 1024) == -1
 

@@ -74,3 +74,27 @@ def test_noalloc_small_batches_and_limit():
     assert oracle.rel_err(host(y), want) < TOL
     lib = tb.library()
     assert lib.tb_linear_noalloc(1, 16, 16, 16, 0, 16, 16, 32, 8, 1 << 16, None) == 8  # beyond 4 MiB
+
+
+def test_noalloc_batched_without_room_for_parts():
+    """32 rows of K = 17408 on 2048 weight rows: x' (2.2 MB) and the partial sums of the batched
+    product's eight parts of K (2.1 MB) together pass the 4 MiB array, so the call takes whole
+    rows (x' only).  Against the oracle on sampled rows, and within the tolerance of the
+    workspace entry point, which takes the parts (another summation order)."""
+    n, k, rows = 2048, 17408, 32
+    assert tb.tb_linear_workspace_bytes("base3", rows, n, k) > (4 << 20) >= 4 * rows * k
+    note(f"noalloc base3 n={n} k={k} rows={rows} without parts")
+    g = synth.rng(290, 7, n % 251, k // 1024)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x = g.standard_normal((rows, k)).astype(np.float32)
+    packed, _ = oracle.pack_base3(t)
+    sample = np.unique(np.concatenate([np.arange(0, n, 17), [n - 1]]))
+    want = oracle.gemv("base3", packed[sample], s[sample], oracle.rotate(x.astype(np.float64), signs), k)
+    pd, sd, xd, sgn = dev(packed), scales_dev(s), dev(x), signs_dev(signs)
+    y0 = torch.full((rows, n), float("nan"), dtype=torch.float32, device="cuda")
+    _noalloc("base3", pd, sd, xd, sgn, y0)
+    a = host(y0)
+    assert oracle.rel_err(a[:, sample], want) < TOL
+    assert oracle.rel_err(a, host(tb.tb_linear_ws("base3", pd, sd, xd, sgn))) < TOL
