@@ -13,6 +13,12 @@
 //     of one group once and uses them for all T tiles, so the activations are
 //     read once per workgroup and the weights once per call.  At the end the
 //     waves' partial sums meet in LDS and are added in wave order.
+//   * Where the caller has room for partial sums, the workgroups of a call
+//     can take K in parts (five tiles each, workgroup w: part w / rb): a part's
+//     workgroups read only that part's activations and write its partial sums,
+//     which a second launch adds in part order.  So rows too few to fill the
+//     compute units with five-tile workgroups do not make every workgroup read
+//     all of the activations for fewer tiles.
 //   * Weight codes become fp16 B operands without a table: a 2-bit code c
 //     moved to bits 10-11 of a half is the fp16 number c * 2^-14 (exponent
 //     field c, mantissa 0: 0, 2^-14, 2^-13), and one AND with 0x0C000C00 takes
