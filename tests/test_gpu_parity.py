@@ -385,6 +385,42 @@ def test_linear_ws_batch1_rows_in_parts(n, k, x_dtype):
     assert np.array_equal(host(tb.tb_linear_ws("base3", pd, sd, xd, sgn, workspace=ws)), got)
 
 
+@pytest.mark.parametrize("packing,n,k,b,parts", [
+    ("base3", 1, 17408, 32, 8),     # one row in a ragged tile, eight parts of 17 groups
+    ("2bit", 17, 2048, 16, 2),      # two parts of 8 groups (two parts only from batch 16)
+    ("base3", 300, 17408, 9, 8),
+    ("base3", 3000, 17408, 8, 6),   # six parts: five of 23 groups, the last of 21
+    ("2bit", 5120, 5120, 8, 4),
+    ("base3", 9000, 5120, 16, 2),
+    ("2bit", 9000, 5120, 9, 1),     # two parts below batch 16 are not taken: whole rows
+])
+def test_linear_ws_batched_parts_of_k(packing, n, k, b, parts):
+    """The batched product in parts of K through tb_linear_ws: where rows are too few for
+    five-tile workgroups on every compute unit, P parts of K (at most 8, at least 8 groups each)
+    on separate workgroups write their partial sums to the workspace after x' (all filled with NaN
+    first: every word must be written) and a second launch adds them in part order.  Every batch
+    row against the oracle (every row up to 4 M weights, else every 7th and the first and last 16);
+    a repeated call on the same workspace gives the same bits."""
+    note(f"tb_linear_ws parts of K {packing} n={n} k={k} b={b} parts={parts}")
+    g = synth.rng(276, 0, n % 251, k // 1024)
+    t = synth.trits(g, n, k)
+    s = synth.scales_f16(g, n, k)
+    signs = synth.sign_bits(g, k)
+    x = g.standard_normal((b, k)).astype(np.float32)
+    packed, _ = PACK_REF[packing](t)
+    rows = np.arange(n) if n * k <= 4_000_000 else \
+        np.unique(np.concatenate([np.arange(0, n, 7), np.arange(16), np.arange(n - 16, n)]))
+    want = oracle.gemv(packing, packed[rows], s[rows], oracle.rotate(x.astype(np.float64), signs), k)
+    need = tb.tb_linear_workspace_bytes(packing, b, n, k)
+    assert need == 4 * b * k + (4 * parts * b * n if parts > 1 else 0)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    pd, sd, xd, sgn = dev(packed), scales_dev(s), dev(x), signs_dev(signs)
+    got = host(tb.tb_linear_ws(packing, pd, sd, xd, sgn, workspace=ws))
+    assert np.isfinite(got).all()
+    assert oracle.rel_err(got[:, rows], want) < TOL
+    assert np.array_equal(host(tb.tb_linear_ws(packing, pd, sd, xd, sgn, workspace=ws)), got)
+
+
 @pytest.mark.parametrize("packing", ["2bit", "base3"])
 @pytest.mark.parametrize("n", [3 * synth.HIDDEN, 2 * synth.FFN], ids=["qkv_15360", "gate_up_34816"])
 def test_concatenated_linears_sampled_rows(packing, n):
