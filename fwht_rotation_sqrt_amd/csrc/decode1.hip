@@ -8,10 +8,11 @@
 // (byte = sum_i (t_i + 1) 3^i, five trits per byte).
 //
 // Design (gfx950, one workgroup per compute unit):
-//  * Streaming.  A wave owns one tile of 16 weight rows and the whole of K.  Each lane issues
-//    every load of its share of the tile (its codes and scales, about 280 bytes at K = 5120) into
-//    registers when the kernel starts, so the whole weight matrix is in flight at once; the
-//    activation prologue runs while the loads are outstanding.
+//  * Streaming.  A wave owns one tile of 16 weight rows and the whole of K.  Each lane loads its
+//    share of the tile (its codes and scales, about 280 bytes at K = 5120) into registers: the
+//    scales and two 64-byte chunks when the kernel starts, then one chunk each time the matrix loop
+//    reaches the chunk two before it, so the weight stream starts at launch and the activation
+//    prologue runs while the first loads are outstanding.
 //  * Matrix cores.  v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 (e2m1) weights and fp6 (e2m3)
 //    activations.  Its four lane groups (16 lanes each, one per 32 K-slots) are made independent:
 //    A row 4q + j (j = 0..3) carries data only in the K-slots of lane group q (the other lanes of
@@ -60,6 +61,7 @@ constexpr int kCopies = 32;          // table copies, one per lane of a half wav
 constexpr int kMaxWaves = 16;
 constexpr int kRotScratch = 1088 * 4;  // a rotating wave's transpose scratch (bytes)
 constexpr int kXGroup = 136;           // floats between 128-groups of x' in LDS: 8 groups fill one scratch
+constexpr int kAhead = 2;              // weight chunks a tile wave has in flight ahead of its matrix loop
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -374,17 +376,41 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
   u32x4 R[kChunks > 0 ? kChunks : 1][4];
   u32x4 Tl[kTailLoads > 0 ? kTailLoads : 1];
   uint32_t S[(G4 + 1) / 2];
+  // Each 16-byte load covers 64 contiguous bytes of 16 rows (the four lane groups of a row read
+  // consecutive pieces of one quarter); the pieces move to their lane group later.  A lane without
+  // a tile, and a load that starts past the part's last group, reads past the buffers (zeros):
+  // every load is issued on every path.
+  // (whole rows: the row geometry as compile-time constants, and no padding groups)
+  const uint32_t row_bytes = PARTS ? rp.row_bytes : uint32_t(kB3GroupBytes * kGroups);
+  const uint32_t srow_bytes = PARTS ? rp.srow_bytes : uint32_t(2 * kGroups);
+  const uint32_t wbytes = uint32_t(n) * row_bytes, sbytes = uint32_t(n) * srow_bytes;
+  const auto wr = rsrc(packed, wbytes);
+  const auto sr = rsrc(scales, sbytes);
+  const uint32_t rrow = has_tile ? uint32_t(row) * row_bytes + (PARTS ? rp.part_off : 0u) : wbytes;
+  const uint32_t lim = uint32_t(kB3GroupBytes * rp.real_groups);
+  auto woff = [&](int o) {
+    if constexpr (!PARTS) return rrow + uint32_t(4 * d0w + o);
+    return uint32_t(4 * d0w + o) < lim ? rrow + uint32_t(4 * d0w + o) : wbytes;
+  };
+  // the loads of chunk m (m == kChunks: the tail loads, if any)
+  auto issue = [&](int m) {
+    if (m < kChunks) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * q + 64 * m + 16 * kb), 0, 0);
+        R[m][q] = u32x4{v[0], v[1], v[2], v[3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTailLoads; ++i) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * kb + 64 * kChunks + 16 * i), 0, 0);
+        Tl[i] = u32x4{v[0], v[1], v[2], v[3]};
+      }
+    }
+    // chunk by chunk in issue order, so that waiting for chunk m leaves the later ones in flight
+    __builtin_amdgcn_sched_barrier(0);
+  };
   {
-    // Each 16-byte load covers 64 contiguous bytes of 16 rows (the four lane groups of a row
-    // read consecutive pieces of one quarter); the pieces move to their lane group later.  A
-    // lane without a tile, and a load that starts past the part's last group, reads past the
-    // buffers (zeros): every load is issued on every path.
-    // (whole rows: the row geometry as compile-time constants, and no padding groups)
-    const uint32_t row_bytes = PARTS ? rp.row_bytes : uint32_t(kB3GroupBytes * kGroups);
-    const uint32_t srow_bytes = PARTS ? rp.srow_bytes : uint32_t(2 * kGroups);
-    const uint32_t wbytes = uint32_t(n) * row_bytes, sbytes = uint32_t(n) * srow_bytes;
-    const auto wr = rsrc(packed, wbytes);
-    const auto sr = rsrc(scales, sbytes);
     // the quarter's G4 scales first (the halves take theirs from them; a padding group's scale
     // reads 0): loads complete in issue order, so a scale issued after the codes could only be
     // used once every code load of the wave had arrived
@@ -395,27 +421,14 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
           !PARTS || G4 * kb + 2 * i < rp.real_groups ? srow + uint32_t(2 * G4 * kb + 4 * i) : sbytes;
       S[i] = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
     }
-    const uint32_t rrow = has_tile ? uint32_t(row) * row_bytes + (PARTS ? rp.part_off : 0u) : wbytes;
-    const uint32_t lim = uint32_t(kB3GroupBytes * rp.real_groups);
-    auto woff = [&](int o) {
-      if constexpr (!PARTS) return rrow + uint32_t(4 * d0w + o);
-      return uint32_t(4 * d0w + o) < lim ? rrow + uint32_t(4 * d0w + o) : wbytes;
-    };
+    // The first kAhead chunks now; chunk c + kAhead when chunk c is moved to its lane groups in the
+    // matrix loop.  With every chunk issued at once, all compute units' requests queue together
+    // and a wave's first chunk lands about as late as its last; with kAhead in flight per wave
+    // (40 KB per compute unit at 17408 x 5120, enough to keep HBM busy) the early chunks land early
+    // (34816 x 5120: 17.5 -> 16.2 us; 17408 x 5120: 10.0 -> 9.8 us).
 #pragma unroll
-    for (int m = 0; m < kChunks; ++m) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * q + 64 * m + 16 * kb), 0, 0);
-        R[m][q] = u32x4{v[0], v[1], v[2], v[3]};
-      }
-      // chunk by chunk in issue order, so that waiting for chunk m leaves the later ones in flight
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < kTailLoads; ++i) {  // the rest of the lane's own dwords
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff(kLaneBytes * kb + 64 * kChunks + 16 * i), 0, 0);
-      Tl[i] = u32x4{v[0], v[1], v[2], v[3]};
-    }
+    for (int m = 0; m < kAhead && m <= kChunks; ++m)
+      if (m < kChunks || kTailLoads > 0) issue(m);
   }
   lds_barrier();  // C
 
@@ -430,6 +443,7 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     // needs one of its dwords, so the matrix loop starts on the first chunks while the later ones
     // are still arriving (waiting for a chunk waits only for the loads issued before it).
     auto fill = [&](int c) {
+      if (c + kAhead <= kChunks && (c + kAhead < kChunks || kTailLoads > 0)) issue(c + kAhead);
       if (c < kChunks) {
         transpose_pieces(R[c]);
 #pragma unroll
