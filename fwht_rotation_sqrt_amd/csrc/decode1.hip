@@ -10,8 +10,8 @@
 // Design (gfx950, one workgroup per compute unit):
 //  * Streaming.  A wave owns one tile of 16 weight rows and the whole of K.  Each lane loads its
 //    share of the tile (its codes and scales, about 280 bytes at K = 5120) into registers: the
-//    scales and two 64-byte chunks when the kernel starts, then one chunk each time the matrix loop
-//    reaches the chunk two before it, so the weight stream starts at launch and the activation
+//    scales and the first 64-byte chunk when the kernel starts, then the next chunk each time the
+//    matrix loop reaches a chunk, so the weight stream starts at launch and the activation
 //    prologue runs while the first loads are outstanding.
 //  * Matrix cores.  v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 (e2m1) weights and fp6 (e2m3)
 //    activations.  Its four lane groups (16 lanes each, one per 32 K-slots) are made independent:
@@ -61,7 +61,7 @@ constexpr int kCopies = 32;          // table copies, one per lane of a half wav
 constexpr int kMaxWaves = 16;
 constexpr int kRotScratch = 1088 * 4;  // a rotating wave's transpose scratch (bytes)
 constexpr int kXGroup = 136;           // floats between 128-groups of x' in LDS: 8 groups fill one scratch
-constexpr int kAhead = 2;              // weight chunks a tile wave has in flight ahead of its matrix loop
+constexpr int kAhead = 1;              // weight chunks a tile wave has in flight ahead of its matrix loop
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -423,9 +423,9 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     }
     // The first kAhead chunks now; chunk c + kAhead when chunk c is moved to its lane groups in the
     // matrix loop.  With every chunk issued at once, all compute units' requests queue together
-    // and a wave's first chunk lands about as late as its last; with kAhead in flight per wave
-    // (40 KB per compute unit at 17408 x 5120, enough to keep HBM busy) the early chunks land early
-    // (34816 x 5120: 17.5 -> 16.2 us; 17408 x 5120: 10.0 -> 9.8 us).
+    // and a wave's first chunk lands about as late as its last; with one chunk ahead per wave
+    // (about 20 KB per compute unit at 17408 x 5120, still enough to keep HBM busy) the early
+    // chunks land early (34816 x 5120: 17.5 -> 15.2 us; two chunks ahead: 16.2, three: 17.6).
 #pragma unroll
     for (int m = 0; m < kAhead && m <= kChunks; ++m)
       if (m < kChunks || kTailLoads > 0) issue(m);
