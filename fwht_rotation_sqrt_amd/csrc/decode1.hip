@@ -30,8 +30,12 @@
 //    hardware conversions), so the absolute error is at most about 2^-16 of the largest |x'| of
 //    the step's 20 activations.  The limb exponent rides in the instruction's E8M0 A scale, so
 //    the four result rows of a lane add up to the group's partial sum with no multiply.
-//  * Records.  A record (group, step) holds the four limbs (24 bytes each) and their E8M0 scales;
-//    it lives in the upper half of a table entry slot (table entry i at 256 i, record i at
+//  * Records.  A record (group, step) holds the four limbs (24 bytes each); each limb carries its
+//    own E8M0 scale code in K-slots 5 and 6 (bits 30..37), which face the empty nibbles of every
+//    weight operand and so add nothing, so a lane reads its limb as 16 + 8 bytes and takes the
+//    scale with one funnel shift.  Records live in the upper half of a table entry slot (table
+//    entry i at 256 i, record i at 256 i + 128), so table and records share one 256-byte-stride
+//    region.
 //    256 i + 128), so table and records share one 256-byte-stride region.
 #include "tb.h"
 #include "tb_internal.hpp"
@@ -51,11 +55,12 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 typedef uint32_t v6u __attribute__((ext_vector_type(6)));
 typedef uint32_t v16u __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSteps = 7;            // 4-byte matrix steps per 26-byte group
 constexpr int kSlot = 256;           // LDS bytes per table entry / record slot
 constexpr int kRecOff = 128;         // record i at kSlot * i + kRecOff
-constexpr int kLimbBytes = 32;       // one limb of a record: 6 dwords of fp6 + E8M0 word + pad
+constexpr int kLimbBytes = 32;       // one limb of a record: 6 dwords of fp6 (scale code in slots 5-6) + pad
 constexpr int kTableEntries = 243;   // base-3 bytes 0..242
 constexpr int kCopies = 32;          // table copies, one per lane of a half wave
 constexpr int kMaxWaves = 16;
@@ -245,9 +250,12 @@ __device__ __forceinline__ void build_record(uint32_t xb, int g, int s, uint32_t
           od[i] = fmaf(-float(__builtin_bit_cast(_Float16, uint16_t(pair >> 16))), sc, od[i]);
       }
     }
+    // the limb's E8M0 code 127 + E - 4j goes into its K-slots 5 and 6 (bits 30..37, zero so far):
+    // every weight operand has empty nibbles there, so the matrix instruction adds nothing for them
     const uint32_t a = rec + uint32_t(kLimbBytes * j);
-    lds_st<u32x4>(a, u32x4{l[0], l[1], l[2], l[3]});
-    lds_st<u32x4>(a + 16, u32x4{l[4], l[5], uint32_t(127 + E - 4 * j), 0u});
+    const uint32_t code = uint32_t(127 + E - 4 * j);
+    lds_st<u32x4>(a, u32x4{l[0] | (code << 30), l[1] | (code >> 2), l[2], l[3]});
+    lds_st<u32x2>(a + 16, u32x2{l[4], l[5]});
   }
 }
 
@@ -483,7 +491,8 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
     // the chunk holding step k's code dword (the tail loads count as the last one)
     auto chunk_of = [&](int k) { return min(step_dword(k) / 16, kChunks); };
     v8i Bq[kPD + 1];
-    u32x4 Alo[kPD + 1], Ahi[kPD + 1];
+    u32x4 Alo[kPD + 1];
+    u32x2 Ahi[kPD + 1];
     auto fetch = [&](int k) {
       const int slot = k % (kPD + 1);
       if (k == 0 || chunk_of(k) != chunk_of(k - 1)) fill(chunk_of(k));
@@ -491,7 +500,7 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
       else Bq[slot] = bop(W[step_dword(k)]);
       const uint32_t ab = a_base + uint32_t(group_of(k)) * a_step + uint32_t(kSlot * (k % kSteps));
       Alo[slot] = lds_ld<u32x4>(ab);
-      Ahi[slot] = lds_ld<u32x4>(ab + 16);
+      Ahi[slot] = lds_ld<u32x2>(ab + 16);
     };
 #pragma unroll
     for (int k = 0; k < kPD; ++k) fetch(k);
@@ -506,7 +515,7 @@ __device__ __forceinline__ void tile_linear(const uint8_t* __restrict__ packed, 
       const v8i a = v8i{int(Alo[slot][0]), int(Alo[slot][1]), int(Alo[slot][2]), int(Alo[slot][3]),
                         int(Ahi[slot][0]), int(Ahi[slot][1]), 0, 0};
       d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, Bq[slot], s == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : d, 2, 4, 0,
-                                                           int(Ahi[slot][2]), 0, 127);
+                                                           int(__builtin_amdgcn_alignbit(Alo[slot][1], Alo[slot][0], 30)), 0, 127);  // A scale: bits 30..37
       if (s == kSteps - 1) {
         const int i = group_of(k);
         const uint32_t sw = S[i >> 1];
