@@ -761,13 +761,9 @@ void run(const uint8_t* packed, const uint16_t* scales, const void* x, const uin
          int k, int parts, hipStream_t s) {
   int grid, per_wg;
   plan(n, parts, grid, per_wg);
-  // two waves per tile (each half of K) while they fit in a workgroup, else one.  With the rotation
-  // at K = 5120, whole rows and five tiles per workgroup one wave per tile is faster (10 waves
-  // instead of 15: the activation waves get more of their SIMDs; 17408 rows 10.35 -> 9.95 us,
-  // 20000 rows 10.6 -> 10.1 us); with four tiles or fewer, x' given, or a row's parts of K (down:
-  // 12.9 -> 13.2 us), two stay faster.
-  const bool two = G4 % 2 == 0 && G4 / 2 >= 1 && (4 * G4) / 8 + 2 * per_wg <= kMaxWaves &&
-                   !(ROT && G4 == 10 && per_wg >= 5 && parts == 1);
+  // two waves per tile (each half of K) while they fit in a workgroup, else one (17408 x 5120 with
+  // the rotation: two 9.5-9.7 us, one 9.9 us)
+  const bool two = G4 % 2 == 0 && G4 / 2 >= 1 && (4 * G4) / 8 + 2 * per_wg <= kMaxWaves;
   // five waves per tile (two groups of each quarter each) where K = 5120 leaves room for them:
   // a workgroup with one or two tiles then runs 14 matrix steps per wave instead of 35 (x' given:
   // 5120 x 5120 7.05 -> 6.4 us; with the rotation in the prologue the extra waves slow the
