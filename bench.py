@@ -335,7 +335,7 @@ def stream_ceiling(per_copy, reps=20):
     _, g = time_graph(large, large)
     t_big = event_time(g, 2) / (reps // 4)
     del g, big
-    return {"kernel": "tb_stream_read (16-byte loads, 8 in flight per lane)",
+    return {"kernel": "tb_stream_read (16-byte loads, 4 in flight per lane)",
             "gbs_at_step_size": round(per_copy // 16 * 16 / t_small / 1e9, 1), "step_size_bytes": per_copy // 16 * 16,
             "us_at_step_size": round(t_small * 1e6, 3),
             "gbs_at_2GB": round(big_bytes / t_big / 1e9, 1)}

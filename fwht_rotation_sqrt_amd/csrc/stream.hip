@@ -1,16 +1,17 @@
 // Read-only HBM stream: the measured ceiling that the weight-streaming products
 // are compared with.  Every byte of the buffer is read once with 16-byte buffer
-// loads, eight in flight per lane; a workgroup folds what it read into one XOR
+// loads, four in flight per lane (one launch over 19.5 MB: 5.2 us with four, 5.4
+// with eight, 5.2 with two, 5.5 with one; over 2 GB four is also the fastest); a workgroup folds what it read into one XOR
 // word and writes it, so the reads cannot be dropped and the writes are
-// negligible (4 bytes per 32 KB read).
+// negligible (4 bytes per 16 KB read).
 #include "tb_internal.hpp"
 
 namespace tb {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;                                   // 16-byte loads in flight per lane
-constexpr uint32_t kChunk = uint32_t(kThreads) * kUnroll * 16;  // bytes per workgroup pass: 32 KB
+constexpr int kUnroll = 4;                                   // 16-byte loads in flight per lane
+constexpr uint32_t kChunk = uint32_t(kThreads) * kUnroll * 16;  // bytes per workgroup pass: 16 KB
 constexpr int kMaxGrid = 8192;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
